@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+One step = one ta_decode call: the split-KV partial-state kernel over the whole
+KV cache, then the tree merge, for every sequence and query head of the
+workload. Default workload: the Llama-3.1-8B attention shape (32 query heads,
+8 KV heads, d = 128), bf16, batch 1, 131072-token context, chunk 2048 (64
+partial states, a 6-level tree), seeded synthetic N(0,1) inputs.
+
+Timing: W untimed warm-up steps, then exactly K steps between two device
+synchronisations, bracketed by HIP events on the stream the kernels run on.
+The step inputs rotate over several resident copies of the cache (at least
+2 GiB in total, far above the 256 MB last-level cache), so every step streams
+its K/V from HBM. The dominant kernel (partial states) is also timed alone with
+events over K launches, for the roofline figure. The CPU oracle is timed on the
+same host over a bounded sample, as a baseline only.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn µs/step + achieved HBM GB/s (% peak), 8B-GQA bf16 128k ctx"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_partial_gqa8b_128k.json")
+PARTIAL_SRC = os.path.join(ROOT, "softmax_tree_reduction_amd", "csrc", "partial.hip")
+
+
+def algorithmic_bytes(wl, seqlens) -> int:
+    """K + V rows of every valid token, q, out (f32) and lse (f32)."""
+    es = 2 if wl.dtype == "bf16" else 4
+    kv = 2 * int(sum(int(n) for n in seqlens)) * wl.Hkv * wl.d * es
+    return kv + wl.B * wl.Hq * wl.d * es + wl.B * wl.Hq * wl.d * 4 + wl.B * wl.Hq * 4
+
+
+def file_sha256(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(wl_name: str):
+    """HBM bytes per partial-kernel launch from the committed rocprofv3 counter runs,
+    or None when they are missing or were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != wl_name or t.get("partial_hip_sha256") != file_sha256(PARTIAL_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, wl, budget_s: float):
+    """The oracle, untouched, on the full step (all rows), repeated within a time budget."""
+    import oracle
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+    first = time.perf_counter() - t0
+    reps = max(1, min(5, int(budget_s / max(first, 1e-3))))
+    times = [first]
+    for _ in range(reps - 1):
+        t0 = time.perf_counter()
+        oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    med = times[len(times) // 2]
+    gbs = algorithmic_bytes(wl, inp.seqlens) / med / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the full step of {wl.name} (all {wl.B * wl.Hq} query rows, {int(sum(inp.seqlens))} tokens "
+                      f"per KV head), float64 two-pass definition, median of {len(times)} runs, "
+                      f"{med * 1e3:.1f} ms per step"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa8b_128k")
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk")
+    ap.add_argument("--min-rotation-bytes", type=float, default=2 * 2**30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this single-GPU decode path has no multi-GPU mode "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import softmax_tree_reduction_amd as ta
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    wl = W.WORKLOADS[args.workload]
+    chunk = args.chunk or wl.chunk
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"bench: generating {wl.name} (seed {args.seed})", file=sys.stderr, flush=True)
+    inp = W.make_decode_inputs(wl, args.seed)
+    step_bytes = algorithmic_bytes(wl, inp.seqlens)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q = to_dev(inp.q)
+    sl = torch.from_numpy(inp.seqlens.astype(np.int32)).to(dev)
+    k0, v0 = to_dev(inp.k), to_dev(inp.v)
+    cache_bytes = k0.numel() * k0.element_size() * 2
+    copies = max(1, math.ceil(args.min_rotation_bytes / cache_bytes))
+    ks, vs = [k0], [v0]
+    for _ in range(copies - 1):
+        ks.append(k0.clone())
+        vs.append(v0.clone())
+    print(f"bench: {copies} resident copies of the {cache_bytes / 2**20:.0f} MiB cache", file=sys.stderr, flush=True)
+
+    # parity of this launch configuration on sampled rows before timing
+    import oracle
+    out, lse = ta.decode(q, k0, v0, sl, chunk=chunk)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(0).choice(wl.B * wl.Hq, size=min(8, wl.B * wl.Hq), replace=False))
+    ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens, rows=rows)
+    o = out.cpu().numpy().reshape(-1, wl.d)[rows]
+    l_ = lse.cpu().numpy().reshape(-1)[rows]
+    tol = 4e-3 if wl.dtype == "bf16" else 1e-5
+    perr = float(np.abs(o - ro).max())
+    lerr = float((np.abs(l_ - rl) / np.maximum(1.0, np.abs(rl))).max())
+    if not (perr <= tol and lerr <= 1e-4):
+        print(f"bench: parity check failed (out err {perr}, lse err {lerr})", file=sys.stderr)
+        return 1
+    print(f"bench: parity on {len(rows)} sampled rows ok (max|out-oracle| {perr:.2e}, lse rel {lerr:.2e})",
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    P = -(-wl.N // chunk)
+
+    # ---- whole step: ta_decode (partial kernel + tree merge)
+    for i in range(args.warmup):
+        ta.decode(q, ks[i % copies], vs[i % copies], sl, chunk=chunk, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        ta.decode(q, ks[i % copies], vs[i % copies], sl, chunk=chunk, out=out, lse=lse)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    print(f"bench: {args.steps} steps, {ms_step * 1e3:.1f} us/step (host wall {wall / args.steps * 1e6:.1f} us/step)",
+          file=sys.stderr, flush=True)
+
+    # ---- dominant kernel alone: ta_partial over the same rotation
+    po = torch.empty(wl.B, wl.Hq, P, wl.d, dtype=torch.float32, device=dev)
+    pl = torch.empty(wl.B, wl.Hq, P, dtype=torch.float32, device=dev)
+    for i in range(args.warmup):
+        ta.partial(q, ks[i % copies], vs[i % copies], sl, chunk=chunk, partial_o=po, partial_lse=pl)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        ta.partial(q, ks[i % copies], vs[i % copies], sl, chunk=chunk, partial_o=po, partial_lse=pl)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_partial = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- merge alone on the partial states
+    for _ in range(args.warmup):
+        ta.combine(po, pl, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        ta.combine(po, pl, out=out, lse=lse)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_combine = ev0.elapsed_time(ev1) / args.steps
+
+    partial_bytes = step_bytes - wl.B * wl.Hq * (wl.d + 1) * 4  # K, V and q; out/lse belong to the merge
+    achieved = partial_bytes / (ms_partial * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name)
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, wl, args.cpu_budget)
+
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d,
+                   "context": wl.N, "chunk": chunk, "partials": P, "tree_levels": math.ceil(math.log2(P)) if P > 1 else 0,
+                   "algorithmic_bytes_per_step": step_bytes, "cache_copies": copies, "seed": args.seed},
+        "kernels_us": {"partial": round(ms_partial * 1e3, 2), "combine": round(ms_combine * 1e3, 2)},
+        "roofline": {"kernel": "partial_kernel", "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": partial_bytes},
+        "parity": {"rows": len(rows), "max_abs_out_err": perr, "max_rel_lse_err": lerr},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

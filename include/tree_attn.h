@@ -1,0 +1,148 @@
+/*
+ * tree_attn.h - C ABI of the single-GPU Tree Attention decode path (gfx950).
+ *
+ * What is computed. One decode step of exact softmax attention: for every
+ * sequence b and query head h, a single query q[b,h,:] attends to the first
+ * n_b keys and values of its KV head,
+ *
+ *     s_j = q . K_j / sqrt(d),   out = sum_j softmax(s)_j V_j,   lse = ln sum_j exp(s_j),
+ *
+ * ("Tree Attention Guide: Topology-Aware LLM Decoding", section "Core
+ * Innovation 2: Mathematical Formulation of Online Softmax on Trees", the
+ * softmax with a global maximum; the 1/sqrt(d) scale is the one the same
+ * page's worker listing applies to its scores). The keys are cut into chunks
+ * of `chunk` tokens. Each chunk yields a partial state (running max m, sum of
+ * exponentials l, weighted value sum o), as in section "Core Innovation 1",
+ * step 2 of that page; the partial states are merged by the page's merge
+ * operator (m = max, rescale by exp(m_A - m) and exp(m_B - m), add) as a
+ * binary tree of depth ceil(log2 P) (section "Core Innovation 1", step 3),
+ * and the root is normalised, O = o / l (end of "Core Innovation 2").
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are passed as host-side ta_tensor descriptors whose `data`
+ *    points to device memory on the current HIP device. The descriptors are
+ *    read during the call only; the library keeps no pointer after it returns.
+ *    The caller owns every tensor.
+ *  - Strides are in elements. The last dimension (the head dimension d) must
+ *    be contiguous (stride 1), and every row start must be 16-byte aligned.
+ *  - Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
+ *  - The log-sum-exp is a natural logarithm. A sequence with no tokens (and a
+ *    partial state of an empty chunk) has out = 0 and lse = -inf.
+ *  - A partial state is stored normalised: o_i = o / l (the softmax-weighted
+ *    mean of V over the chunk) and lse_i = m + ln l. This is the same state as
+ *    the page's (o, l, m): (o_i, 1, lse_i) merges exactly like it.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream) and the call returns without waiting for it. Inputs must stay
+ *    valid and unmodified until the stream reaches the work.
+ *  - Outputs must not alias inputs.
+ *  - Results are bitwise reproducible for the same inputs, shapes and chunk
+ *    (fixed reduction order, no atomics).
+ *
+ * Errors: a negative return code means nothing was enqueued (argument
+ * validation happens before any launch) or, for TA_ERR_HIP, that the HIP
+ * runtime refused an allocation or a launch. ta_last_error() returns a
+ * message for the most recent non-zero return on the calling thread.
+ * Faults during execution surface on the stream, as for any HIP kernel.
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TA_MAX_DIMS 4
+
+typedef enum ta_dtype {
+    TA_F32 = 0,   /* IEEE binary32 */
+    TA_BF16 = 1   /* bfloat16: the upper 16 bits of a binary32 */
+} ta_dtype;
+
+typedef struct ta_tensor {
+    void* data;                    /* device pointer */
+    int32_t dtype;                 /* ta_dtype */
+    int32_t ndim;                  /* number of used entries in shape/stride */
+    int64_t shape[TA_MAX_DIMS];
+    int64_t stride[TA_MAX_DIMS];   /* in elements */
+} ta_tensor;
+
+enum {
+    TA_OK = 0,
+    TA_ERR_NULL = -1,         /* a required pointer or descriptor is NULL */
+    TA_ERR_SHAPE = -2,        /* wrong ndim, or shapes that do not agree */
+    TA_ERR_DTYPE = -3,        /* unsupported or mismatched dtype */
+    TA_ERR_STRIDE = -4,       /* d not contiguous, or a row not 16-byte aligned */
+    TA_ERR_ARG = -5,          /* chunk < 1, n_parts out of range, ... */
+    TA_ERR_UNSUPPORTED = -6,  /* a head dimension or size this build has no kernel for */
+    TA_ERR_HIP = -7           /* the HIP runtime returned an error */
+};
+
+/*
+ * ta_decode - one decode step: partial states per chunk, tree merge, output.
+ *
+ *   q        [B, Hq, d]      bf16 or f32 (the query of every head)
+ *   k, v     [B, Hkv, N, d]  same dtype as q; N is the cache capacity per sequence
+ *   seqlens  device int32[B], the number of valid tokens of each sequence
+ *            (0 <= n_b <= N; values outside are clamped to that range), or
+ *            NULL for n_b = N. Keys and values at or past n_b are never read.
+ *   out      [B, Hq, d]      f32, the attention output
+ *   lse      [B, Hq]         f32, natural-log log-sum-exp of the logits, or NULL
+ *   chunk    tokens per partial state, >= 1
+ *
+ * Supported: d in {64, 128}; Hq a multiple of Hkv; B <= 65535; Hq <= 65535.
+ * Needs Hq * P * (d + 1) * 4 bytes of stream-ordered device workspace per
+ * sequence (P = ceil(N / chunk)), allocated and released on `stream` by the
+ * library (hipMallocAsync / hipFreeAsync).
+ */
+int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v,
+              const int32_t* seqlens, const ta_tensor* out, const ta_tensor* lse,
+              int32_t chunk, void* stream);
+
+/*
+ * ta_combine - merge n_parts partial states per row by the binary tree, then
+ * normalise ("Core Innovation 1" step 3 and "Core Innovation 2" of the page).
+ *
+ *   partial_o    [B, H, P, d] f32 (normalised partial outputs o_i)
+ *   partial_lse  [B, H, P]    f32 (natural-log lse_i; -inf marks an empty state,
+ *                whose o_i is then ignored)
+ *   n_parts      number of leading states to merge, 0 <= n_parts <= P
+ *                (0 gives out = 0, lse = -inf)
+ *   out          [B, H, d] f32;  lse [B, H] f32 or NULL
+ *
+ * Leaf i covers the i-th state; level t of the tree merges node i with node
+ * i + 2^t for every i that is a multiple of 2^(t+1) (a node without a partner
+ * passes up unchanged), giving ceil(log2 n_parts) levels.
+ * Supported: d in {64, 128}. n_parts above 128 (d = 128) or 256 (d = 64) runs
+ * the same tree in several launches and takes stream-ordered workspace.
+ */
+int ta_combine(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts,
+               const ta_tensor* out, const ta_tensor* lse, void* stream);
+
+/*
+ * ta_partial - the per-chunk partial states alone (the first half of ta_decode).
+ *
+ * Arguments as for ta_decode, with the outputs
+ *   partial_o    [B, Hq, P, d] f32, P >= ceil(N / chunk)
+ *   partial_lse  [B, Hq, P]    f32
+ * Chunk i of sequence b covers tokens [i*chunk, min((i+1)*chunk, n_b)); a
+ * chunk with no tokens gets o_i = 0 and lse_i = -inf. Entries i >= ceil(N/chunk)
+ * are not written. ta_combine over these P states equals ta_decode.
+ * Allocates nothing.
+ */
+int ta_partial(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v,
+               const int32_t* seqlens, const ta_tensor* partial_o, const ta_tensor* partial_lse,
+               int32_t chunk, void* stream);
+
+/* Message for the last non-zero return on this thread ("" if none). Never NULL. */
+const char* ta_last_error(void);
+
+/* ABI version, currently 1. */
+int ta_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

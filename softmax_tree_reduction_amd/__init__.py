@@ -1,0 +1,185 @@
+"""Python binding of libtreeattn.so: single-GPU Tree Attention decode on gfx950.
+
+Argument marshalling only. Every step of the computation runs in the HIP
+kernels behind the C ABI of include/tree_attn.h; torch supplies device memory
+and streams. If the library is not built, every call raises: there is no
+fallback path.
+
+    out, lse = decode(q, k, v, seqlens=None, chunk=2048)
+    po, pl   = partial(q, k, v, seqlens=None, chunk=2048)
+    out, lse = combine(po, pl, n_parts=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = ["decode", "partial", "combine", "TreeAttnError", "library_path", "load_library",
+           "TA_OK", "TA_ERR_NULL", "TA_ERR_SHAPE", "TA_ERR_DTYPE", "TA_ERR_STRIDE", "TA_ERR_ARG",
+           "TA_ERR_UNSUPPORTED", "TA_ERR_HIP", "TaTensor", "EXPORTS"]
+
+TA_OK, TA_ERR_NULL, TA_ERR_SHAPE, TA_ERR_DTYPE, TA_ERR_STRIDE, TA_ERR_ARG, TA_ERR_UNSUPPORTED, TA_ERR_HIP = \
+    0, -1, -2, -3, -4, -5, -6, -7
+TA_F32, TA_BF16 = 0, 1
+EXPORTS = ("ta_decode", "ta_combine", "ta_partial", "ta_last_error", "ta_version")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libtreeattn.so")
+_lock = threading.Lock()
+_lib = None
+
+
+class TreeAttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"tree_attn error {code}: {message}")
+        self.code = code
+
+
+class TaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+    @classmethod
+    def make(cls, data: int, dtype: int, shape, stride) -> "TaTensor":
+        t = cls()
+        t.data = data
+        t.dtype = dtype
+        t.ndim = len(shape)
+        for i, (s, st) in enumerate(zip(shape, stride)):
+            t.shape[i] = int(s)
+            t.stride[i] = int(st)
+        return t
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libtreeattn.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(f"{_LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+            lib = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.POINTER(TaTensor)
+            vp, i32 = ctypes.c_void_p, ctypes.c_int32
+            lib.ta_decode.argtypes = [P, P, P, vp, P, P, i32, vp]
+            lib.ta_partial.argtypes = [P, P, P, vp, P, P, i32, vp]
+            lib.ta_combine.argtypes = [P, P, i32, P, P, vp]
+            for f in (lib.ta_decode, lib.ta_partial, lib.ta_combine):
+                f.restype = ctypes.c_int
+            lib.ta_last_error.restype = ctypes.c_char_p
+            lib.ta_version.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != TA_OK:
+        msg = load_library().ta_last_error().decode(errors="replace")
+        raise TreeAttnError(rc, msg)
+
+
+# ----------------------------------------------------------------------------
+# torch glue (imported lazily so the CPU-side ABI tests need no GPU)
+# ----------------------------------------------------------------------------
+
+def _desc(t) -> TaTensor:
+    import torch
+    if t.dtype == torch.float32:
+        dt = TA_F32
+    elif t.dtype == torch.bfloat16:
+        dt = TA_BF16
+    else:
+        raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    return TaTensor.make(t.data_ptr(), dt, t.shape, t.stride())
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _seqlens_ptr(seqlens, B, device):
+    import torch
+    if seqlens is None:
+        return None, None
+    if not (seqlens.is_cuda and seqlens.dtype == torch.int32 and seqlens.is_contiguous() and seqlens.numel() == B):
+        raise ValueError("seqlens must be a contiguous int32 CUDA tensor with one entry per sequence")
+    if seqlens.device != device:
+        raise ValueError("seqlens must be on the same device as q")
+    return ctypes.c_void_p(seqlens.data_ptr()), seqlens
+
+
+def _same_device(*ts):
+    dev = ts[0].device
+    for t in ts[1:]:
+        if t is not None and t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def decode(q, k, v, seqlens=None, chunk: int = 2048, out=None, lse=None, stream=None):
+    """One decode step: returns (out [B, Hq, d] f32, lse [B, Hq] f32)."""
+    import torch
+    dev = _same_device(q, k, v, out, lse)
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    sl, _keep = _seqlens_ptr(seqlens, B, dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        args = [_desc(q), _desc(k), _desc(v)]
+        o_d, l_d = _desc(out), _desc(lse)
+        _check(lib.ta_decode(*[ctypes.byref(a) for a in args], sl, ctypes.byref(o_d), ctypes.byref(l_d),
+                             int(chunk), _stream_handle(stream, dev)))
+    return out, lse
+
+
+def partial(q, k, v, seqlens=None, chunk: int = 2048, partial_o=None, partial_lse=None, stream=None):
+    """Per-chunk partial states: returns (partial_o [B, Hq, P, d], partial_lse [B, Hq, P]), f32."""
+    import torch
+    dev = _same_device(q, k, v, partial_o, partial_lse)
+    B, Hq, d = q.shape
+    N = k.shape[2]
+    P = max(1, -(-N // int(chunk))) if chunk > 0 else 1
+    if partial_o is None:
+        partial_o = torch.empty(B, Hq, P, d, dtype=torch.float32, device=dev)
+    if partial_lse is None:
+        partial_lse = torch.empty(B, Hq, P, dtype=torch.float32, device=dev)
+    sl, _keep = _seqlens_ptr(seqlens, B, dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        args = [_desc(q), _desc(k), _desc(v)]
+        po_d, pl_d = _desc(partial_o), _desc(partial_lse)
+        _check(lib.ta_partial(*[ctypes.byref(a) for a in args], sl, ctypes.byref(po_d), ctypes.byref(pl_d),
+                              int(chunk), _stream_handle(stream, dev)))
+    return partial_o, partial_lse
+
+
+def combine(partial_o, partial_lse, n_parts=None, out=None, lse=None, stream=None):
+    """Tree merge of partial states: returns (out [B, H, d] f32, lse [B, H] f32)."""
+    import torch
+    dev = _same_device(partial_o, partial_lse, out, lse)
+    B, H, P, d = partial_o.shape
+    if n_parts is None:
+        n_parts = P
+    if out is None:
+        out = torch.empty(B, H, d, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        po_d, pl_d, o_d, l_d = _desc(partial_o), _desc(partial_lse), _desc(out), _desc(lse)
+        _check(lib.ta_combine(ctypes.byref(po_d), ctypes.byref(pl_d), int(n_parts), ctypes.byref(o_d),
+                              ctypes.byref(l_d), _stream_handle(stream, dev)))
+    return out, lse

@@ -1,0 +1,347 @@
+// The C ABI declared in include/tree_attn.h: descriptor validation, dispatch to
+// the partial-state and tree-merge kernels, and stream-ordered workspace.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "../../include/tree_attn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return TA_OK;
+}
+
+int64_t elem_size(int32_t dtype) { return dtype == TA_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks ndim, dtype, a contiguous last dimension, and 16-byte aligned rows.
+int check_tensor(const ta_tensor* t, const char* name, int ndim, bool need_rows_aligned) {
+    if (!t) return fail(TA_ERR_NULL, "%s: descriptor is NULL", name);
+    if (!t->data) return fail(TA_ERR_NULL, "%s: data pointer is NULL", name);
+    if (t->ndim != ndim) return fail(TA_ERR_SHAPE, "%s: expected %d dimensions, got %d", name, ndim, t->ndim);
+    if (t->dtype != TA_F32 && t->dtype != TA_BF16) return fail(TA_ERR_DTYPE, "%s: unknown dtype %d", name, t->dtype);
+    for (int i = 0; i < ndim; ++i) {
+        if (t->shape[i] < 0) return fail(TA_ERR_SHAPE, "%s: negative size in dimension %d", name, i);
+        if (t->stride[i] < 0) return fail(TA_ERR_STRIDE, "%s: negative stride in dimension %d", name, i);
+    }
+    if (t->shape[ndim - 1] > 1 && t->stride[ndim - 1] != 1)
+        return fail(TA_ERR_STRIDE, "%s: the last dimension must be contiguous (stride 1), got %lld", name,
+                    (long long)t->stride[ndim - 1]);
+    if (need_rows_aligned) {
+        if (!aligned16(t->data)) return fail(TA_ERR_STRIDE, "%s: data pointer is not 16-byte aligned", name);
+        const int64_t es = elem_size(t->dtype);
+        for (int i = 0; i < ndim - 1; ++i)
+            if (t->shape[i] > 1 && (t->stride[i] * es) % 16 != 0)
+                return fail(TA_ERR_STRIDE, "%s: stride of dimension %d (%lld elements) is not a multiple of 16 bytes",
+                            name, i, (long long)t->stride[i]);
+    }
+    return TA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(TA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Keep freed workspace in the device's default pool between calls.
+void keep_pool_cached(int device) {
+    static std::mutex mu;
+    static bool done[64] = {};
+    if (device < 0 || device >= 64) return;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done[device]) return;
+    hipMemPool_t pool;
+    if (hipDeviceGetDefaultMemPool(&pool, device) == hipSuccess) {
+        uint64_t threshold = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
+    }
+    done[device] = true;
+}
+
+struct DecodeShape {
+    int64_t B, Hq, Hkv, N, d;
+    ta::Dtype dt;
+};
+
+int check_decode_inputs(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, int32_t chunk, DecodeShape* s) {
+    int rc;
+    if ((rc = check_tensor(q, "q", 3, true)) != TA_OK) return rc;
+    if ((rc = check_tensor(k, "k", 4, true)) != TA_OK) return rc;
+    if ((rc = check_tensor(v, "v", 4, true)) != TA_OK) return rc;
+    if (k->dtype != q->dtype || v->dtype != q->dtype)
+        return fail(TA_ERR_DTYPE, "q, k and v must share a dtype (got %d, %d, %d)", q->dtype, k->dtype, v->dtype);
+    for (int i = 0; i < 4; ++i)
+        if (k->shape[i] != v->shape[i]) return fail(TA_ERR_SHAPE, "k and v shapes differ in dimension %d", i);
+    s->B = q->shape[0];
+    s->Hq = q->shape[1];
+    s->d = q->shape[2];
+    s->Hkv = k->shape[1];
+    s->N = k->shape[2];
+    s->dt = q->dtype == TA_BF16 ? ta::Dtype::BF16 : ta::Dtype::F32;
+    if (k->shape[0] != s->B) return fail(TA_ERR_SHAPE, "k batch %lld != q batch %lld", (long long)k->shape[0], (long long)s->B);
+    if (k->shape[3] != s->d) return fail(TA_ERR_SHAPE, "k head dim %lld != q head dim %lld", (long long)k->shape[3], (long long)s->d);
+    if (s->Hkv <= 0 || s->Hq <= 0 || s->Hq % s->Hkv != 0)
+        return fail(TA_ERR_SHAPE, "query heads (%lld) must be a positive multiple of KV heads (%lld)", (long long)s->Hq,
+                    (long long)s->Hkv);
+    if (s->d != 64 && s->d != 128) return fail(TA_ERR_UNSUPPORTED, "head dimension %lld: supported are 64 and 128", (long long)s->d);
+    if (chunk < 1) return fail(TA_ERR_ARG, "chunk must be >= 1, got %d", chunk);
+    if (s->B > 65535) return fail(TA_ERR_UNSUPPORTED, "batch %lld exceeds 65535", (long long)s->B);
+    if (s->Hq > 65535) return fail(TA_ERR_UNSUPPORTED, "query heads %lld exceed 65535", (long long)s->Hq);
+    if (s->N > INT32_MAX - chunk) return fail(TA_ERR_UNSUPPORTED, "cache length %lld too large", (long long)s->N);
+    return TA_OK;
+}
+
+int check_partials(const ta_tensor* po, const ta_tensor* pl, int64_t B, int64_t H, int64_t d, int64_t min_parts,
+                   const char* po_name, const char* pl_name) {
+    int rc;
+    if ((rc = check_tensor(po, po_name, 4, true)) != TA_OK) return rc;
+    if ((rc = check_tensor(pl, pl_name, 3, false)) != TA_OK) return rc;
+    if (po->dtype != TA_F32 || pl->dtype != TA_F32) return fail(TA_ERR_DTYPE, "%s and %s must be f32", po_name, pl_name);
+    if (po->shape[0] != B || po->shape[1] != H || po->shape[3] != d)
+        return fail(TA_ERR_SHAPE, "%s must be [%lld, %lld, P, %lld]", po_name, (long long)B, (long long)H, (long long)d);
+    if (pl->shape[0] != B || pl->shape[1] != H || pl->shape[2] != po->shape[2])
+        return fail(TA_ERR_SHAPE, "%s must be [%lld, %lld, %lld]", pl_name, (long long)B, (long long)H, (long long)po->shape[2]);
+    if (po->shape[2] < min_parts)
+        return fail(TA_ERR_SHAPE, "%s holds %lld partial states, needs %lld", po_name, (long long)po->shape[2], (long long)min_parts);
+    return TA_OK;
+}
+
+int check_outputs(const ta_tensor* out, const ta_tensor* lse, int64_t B, int64_t H, int64_t d) {
+    int rc;
+    if ((rc = check_tensor(out, "out", 3, true)) != TA_OK) return rc;
+    if (out->dtype != TA_F32) return fail(TA_ERR_DTYPE, "out must be f32");
+    if (out->shape[0] != B || out->shape[1] != H || out->shape[2] != d)
+        return fail(TA_ERR_SHAPE, "out must be [%lld, %lld, %lld]", (long long)B, (long long)H, (long long)d);
+    if (lse) {
+        if ((rc = check_tensor(lse, "lse", 2, false)) != TA_OK) return rc;
+        if (lse->dtype != TA_F32) return fail(TA_ERR_DTYPE, "lse must be f32");
+        if (lse->shape[0] != B || lse->shape[1] != H)
+            return fail(TA_ERR_SHAPE, "lse must be [%lld, %lld]", (long long)B, (long long)H);
+    }
+    return TA_OK;
+}
+
+// Heads per workgroup: the largest of 8, 4, 2, 1 that divides the GQA group.
+int heads_per_wg(int64_t group) {
+    for (int g : {8, 4, 2, 1})
+        if (group % g == 0) return g;
+    return 1;
+}
+
+ta::PartialParams partial_params(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const int32_t* seqlens,
+                                 float* po, const int64_t po_st[3], float* pl, const int64_t pl_st[3],
+                                 const DecodeShape& s, int32_t chunk) {
+    ta::PartialParams p{};
+    p.q = q->data;
+    p.k = k->data;
+    p.v = v->data;
+    p.seqlens = seqlens;
+    p.po = po;
+    p.plse = pl;
+    p.q_sb = q->stride[0];
+    p.q_sh = q->stride[1];
+    p.k_sb = k->stride[0];
+    p.k_sh = k->stride[1];
+    p.k_st = k->stride[2];
+    p.v_sb = v->stride[0];
+    p.v_sh = v->stride[1];
+    p.v_st = v->stride[2];
+    p.po_sb = po_st[0];
+    p.po_sh = po_st[1];
+    p.po_sp = po_st[2];
+    p.pl_sb = pl_st[0];
+    p.pl_sh = pl_st[1];
+    p.pl_sp = pl_st[2];
+    p.N = (int32_t)s.N;
+    p.chunk = chunk;
+    p.group = (int32_t)(s.Hq / s.Hkv);
+    p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.d));
+    return p;
+}
+
+// Runs the merge tree over n_parts leaves per row and writes (out, lse).
+// Rows with more leaves than one workgroup takes go through intermediate levels
+// held in stream-ordered workspace.
+int run_combine(const float* po, const int64_t po_st[3], const float* pl, const int64_t pl_st[3], int64_t n_parts,
+                const int32_t* seqlens, int32_t chunk, int64_t N, int64_t B, int64_t H, int64_t d, float* out,
+                const int64_t out_st[2], float* lse, const int64_t lse_st[2], hipStream_t stream) {
+    const int64_t span = ta::combine_max_leaves((int)d);
+    const float* cur_o = po;
+    const float* cur_l = pl;
+    int64_t cur_po[3] = {po_st[0], po_st[1], po_st[2]};
+    int64_t cur_pl[3] = {pl_st[0], pl_st[1], pl_st[2]};
+    int64_t leaves = n_parts;
+    const int32_t* sl = seqlens;
+    void* scratch[2] = {nullptr, nullptr};
+    int which = 0;
+    int rc = TA_OK;
+    hipError_t e = hipSuccess;
+
+    while (leaves > span) {
+        const int64_t groups = (leaves + span - 1) / span;
+        const size_t bytes = (size_t)(B * H * groups * (d + 1)) * sizeof(float);
+        if (scratch[which]) {
+            (void)hipFreeAsync(scratch[which], stream);
+            scratch[which] = nullptr;
+        }
+        if ((e = hipMallocAsync(&scratch[which], bytes, stream)) != hipSuccess) {
+            rc = hip_fail(e, "hipMallocAsync (merge workspace)");
+            break;
+        }
+        float* nxt_o = static_cast<float*>(scratch[which]);
+        float* nxt_l = nxt_o + B * H * groups * d;
+        ta::CombineParams c{};
+        c.po = cur_o;
+        c.plse = cur_l;
+        c.po_sb = cur_po[0]; c.po_sh = cur_po[1]; c.po_sp = cur_po[2];
+        c.pl_sb = cur_pl[0]; c.pl_sh = cur_pl[1]; c.pl_sp = cur_pl[2];
+        c.n_parts = (int32_t)leaves;
+        c.seqlens = sl;
+        c.chunk = chunk;
+        c.N = (int32_t)N;
+        c.out = nxt_o;
+        c.lse = nxt_l;
+        c.out_sb = H * groups * d; c.out_sh = groups * d; c.out_sg = d;
+        c.lse_sb = H * groups; c.lse_sh = groups; c.lse_sg = 1;
+        if ((e = ta::launch_combine_pass(c, (int)d, (int)B, (int)H, (int)groups, (int)span, stream)) != hipSuccess) {
+            rc = hip_fail(e, "merge kernel launch");
+            break;
+        }
+        cur_o = nxt_o;
+        cur_l = nxt_l;
+        cur_po[0] = c.out_sb; cur_po[1] = c.out_sh; cur_po[2] = c.out_sg;
+        cur_pl[0] = c.lse_sb; cur_pl[1] = c.lse_sh; cur_pl[2] = c.lse_sg;
+        leaves = groups;
+        sl = nullptr;  // empty groups were written as empty states
+        which ^= 1;
+    }
+    if (rc == TA_OK) {
+        ta::CombineParams c{};
+        c.po = cur_o;
+        c.plse = cur_l;
+        c.po_sb = cur_po[0]; c.po_sh = cur_po[1]; c.po_sp = cur_po[2];
+        c.pl_sb = cur_pl[0]; c.pl_sh = cur_pl[1]; c.pl_sp = cur_pl[2];
+        c.n_parts = (int32_t)leaves;
+        c.seqlens = sl;
+        c.chunk = chunk;
+        c.N = (int32_t)N;
+        c.out = out;
+        c.lse = lse;
+        c.out_sb = out_st[0]; c.out_sh = out_st[1]; c.out_sg = 0;
+        c.lse_sb = lse ? lse_st[0] : 0; c.lse_sh = lse ? lse_st[1] : 0; c.lse_sg = 0;
+        if ((e = ta::launch_combine_pass(c, (int)d, (int)B, (int)H, 1, (int)(leaves > 0 ? leaves : 1), stream)) != hipSuccess)
+            rc = hip_fail(e, "merge kernel launch");
+    }
+    for (void* s : scratch)
+        if (s) (void)hipFreeAsync(s, stream);
+    return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ta_version(void) { return 1; }
+
+const char* ta_last_error(void) { return g_last_error.c_str(); }
+
+int ta_partial(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const int32_t* seqlens,
+               const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t chunk, void* stream) {
+    DecodeShape s;
+    int rc;
+    if ((rc = check_decode_inputs(q, k, v, chunk, &s)) != TA_OK) return rc;
+    const int64_t P = (s.N + chunk - 1) / chunk;
+    if ((rc = check_partials(partial_o, partial_lse, s.B, s.Hq, s.d, P, "partial_o", "partial_lse")) != TA_OK) return rc;
+    if (s.B == 0 || P == 0) return ok();
+    const int gt = heads_per_wg(s.Hq / s.Hkv);
+    ta::PartialParams p = partial_params(q, k, v, seqlens, static_cast<float*>(partial_o->data), partial_o->stride,
+                                         static_cast<float*>(partial_lse->data), partial_lse->stride, s, chunk);
+    hipError_t e = ta::launch_partial(p, s.dt, (int)s.d, gt, (int)s.B, (int)s.Hq, (int)P, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "partial kernel launch");
+    return ok();
+}
+
+int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const int32_t* seqlens,
+              const ta_tensor* out, const ta_tensor* lse, int32_t chunk, void* stream) {
+    DecodeShape s;
+    int rc;
+    if ((rc = check_decode_inputs(q, k, v, chunk, &s)) != TA_OK) return rc;
+    if ((rc = check_outputs(out, lse, s.B, s.Hq, s.d)) != TA_OK) return rc;
+    if (s.B == 0) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t P = s.N > 0 ? (s.N + chunk - 1) / chunk : 1;  // N = 0: one empty state per row
+    const size_t bytes = (size_t)(s.B * s.Hq * P * (s.d + 1)) * sizeof(float);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    keep_pool_cached(dev);
+    void* ws = nullptr;
+    if ((e = hipMallocAsync(&ws, bytes, st)) != hipSuccess) return hip_fail(e, "hipMallocAsync (partial states)");
+    float* po = static_cast<float*>(ws);
+    float* pl = po + s.B * s.Hq * P * s.d;
+    const int64_t po_st[3] = {s.Hq * P * s.d, P * s.d, s.d};
+    const int64_t pl_st[3] = {s.Hq * P, P, 1};
+    const int gt = heads_per_wg(s.Hq / s.Hkv);
+    ta::PartialParams p = partial_params(q, k, v, seqlens, po, po_st, pl, pl_st, s, chunk);
+    if ((e = ta::launch_partial(p, s.dt, (int)s.d, gt, (int)s.B, (int)s.Hq, (int)P, st)) != hipSuccess) {
+        (void)hipFreeAsync(ws, st);
+        return hip_fail(e, "partial kernel launch");
+    }
+    const int64_t out_st[2] = {out->stride[0], out->stride[1]};
+    const int64_t lse_st[2] = {lse ? lse->stride[0] : 0, lse ? lse->stride[1] : 0};
+    rc = run_combine(po, po_st, pl, pl_st, P, seqlens, chunk, s.N, s.B, s.Hq, s.d, static_cast<float*>(out->data),
+                     out_st, lse ? static_cast<float*>(lse->data) : nullptr, lse_st, st);
+    (void)hipFreeAsync(ws, st);
+    if (rc != TA_OK) return rc;
+    return ok();
+}
+
+int ta_combine(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts, const ta_tensor* out,
+               const ta_tensor* lse, void* stream) {
+    int rc;
+    if (!partial_o) return fail(TA_ERR_NULL, "partial_o: descriptor is NULL");
+    if (partial_o->ndim != 4) return fail(TA_ERR_SHAPE, "partial_o: expected 4 dimensions, got %d", partial_o->ndim);
+    const int64_t B = partial_o->shape[0], H = partial_o->shape[1], d = partial_o->shape[3];
+    if ((rc = check_partials(partial_o, partial_lse, B, H, d, 0, "partial_o", "partial_lse")) != TA_OK) return rc;
+    if (d != 64 && d != 128) return fail(TA_ERR_UNSUPPORTED, "head dimension %lld: supported are 64 and 128", (long long)d);
+    if (n_parts < 0 || n_parts > partial_o->shape[2])
+        return fail(TA_ERR_ARG, "n_parts %d outside [0, %lld]", n_parts, (long long)partial_o->shape[2]);
+    if ((rc = check_outputs(out, lse, B, H, d)) != TA_OK) return rc;
+    if (B > 65535) return fail(TA_ERR_UNSUPPORTED, "batch %lld exceeds 65535", (long long)B);
+    if (B == 0 || H == 0) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (n_parts > ta::combine_max_leaves((int)d)) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        keep_pool_cached(dev);
+    }
+    const int64_t out_st[2] = {out->stride[0], out->stride[1]};
+    const int64_t lse_st[2] = {lse ? lse->stride[0] : 0, lse ? lse->stride[1] : 0};
+    rc = run_combine(static_cast<const float*>(partial_o->data), partial_o->stride,
+                     static_cast<const float*>(partial_lse->data), partial_lse->stride, n_parts, nullptr, 1, 0, B, H, d,
+                     static_cast<float*>(out->data), out_st, lse ? static_cast<float*>(lse->data) : nullptr, lse_st, st);
+    if (rc != TA_OK) return rc;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,320 @@
+// Split-KV partial-state kernel for gfx950.
+//
+// Computes, for one chunk of the KV cache and the G query heads that share its
+// KV head, the partial state of section "Core Innovation 1" step 2 of "Tree
+// Attention Guide: Topology-Aware LLM Decoding": the maximum logit m, the sum of
+// exponentials l = sum exp(s_j - m) and the weighted sum o = sum exp(s_j - m) V_j,
+// with s_j = q . K_j / sqrt(d). It writes the state normalised, (o / l, m + ln l).
+//
+// Layout of the work (one workgroup = one chunk x one head group x one sequence):
+//  - A K or V row of d elements is 256 bytes for bf16 d = 128 (or f32 d = 64). A
+//    wave reads it as 16-byte segments, one per lane, so SEGS = row / 16 lanes hold
+//    one row and a wave-wide load covers RG = 64 / SEGS consecutive rows (1 KB,
+//    fully coalesced). Each lane keeps its segment of q for every head of the group.
+//  - Per token, each lane forms the partial dot products of its segment with the G
+//    query segments (bf16 pairs through v_dot2_f32_bf16), and a DPP butterfly inside
+//    the SEGS-lane row sums them: the whole row group then knows the G logits.
+//  - The running max, the rescale of the accumulators and the exponentials follow
+//    the page's merge operator, once per block of TPL tokens per lane, in base 2
+//    (exp(x) = 2^(x log2 e), the log2 e folded into the logit scale).
+//  - V rows arrive in the same lane layout, so each lane accumulates the G heads
+//    for its own 16-byte slice of channels: no cross-lane traffic on the V side.
+//  - The K/V rows of one block are in flight while the previous block is computed
+//    (two register buffers per lane). The GQA group shares every byte read: each
+//    K/V element is loaded once and used by all G heads.
+//  - Each wave walks the chunk in blocks of RG x TPL tokens, interleaved with the
+//    other waves. At the end the row groups of a wave, then the waves, are merged
+//    with the same operator (shuffles, then LDS) and the state is written.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace ta {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct Storage;
+template <>
+struct Storage<uint16_t> {  // bfloat16 bits
+    static constexpr int kElems = 8;
+};
+template <>
+struct Storage<float> {
+    static constexpr int kElems = 4;
+};
+
+// Partial dot product of one 16-byte segment of q with one of K.
+template <typename T>
+__device__ __forceinline__ float seg_dot(const uint4& qs, const uint4& ks);
+
+template <>
+__device__ __forceinline__ float seg_dot<uint16_t>(const uint4& qs, const uint4& ks) {
+    float acc = 0.0f;
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qs.x), __builtin_bit_cast(bf16x2, ks.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qs.y), __builtin_bit_cast(bf16x2, ks.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qs.z), __builtin_bit_cast(bf16x2, ks.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qs.w), __builtin_bit_cast(bf16x2, ks.w), acc, false);
+    return acc;
+}
+
+template <>
+__device__ __forceinline__ float seg_dot<float>(const uint4& qs, const uint4& ks) {
+    float acc = __uint_as_float(qs.x) * __uint_as_float(ks.x);
+    acc = fmaf(__uint_as_float(qs.y), __uint_as_float(ks.y), acc);
+    acc = fmaf(__uint_as_float(qs.z), __uint_as_float(ks.z), acc);
+    acc = fmaf(__uint_as_float(qs.w), __uint_as_float(ks.w), acc);
+    return acc;
+}
+
+// Widen one 16-byte segment of V to float.
+template <typename T>
+__device__ __forceinline__ void seg_widen(const uint4& s, float (&f)[Storage<T>::kElems]);
+
+template <>
+__device__ __forceinline__ void seg_widen<uint16_t>(const uint4& s, float (&f)[8]) {
+    f[0] = bf16_lo(s.x); f[1] = bf16_hi(s.x);
+    f[2] = bf16_lo(s.y); f[3] = bf16_hi(s.y);
+    f[4] = bf16_lo(s.z); f[5] = bf16_hi(s.z);
+    f[6] = bf16_lo(s.w); f[7] = bf16_hi(s.w);
+}
+
+template <>
+__device__ __forceinline__ void seg_widen<float>(const uint4& s, float (&f)[4]) {
+    f[0] = __uint_as_float(s.x); f[1] = __uint_as_float(s.y);
+    f[2] = __uint_as_float(s.z); f[3] = __uint_as_float(s.w);
+}
+
+__device__ __forceinline__ const uint4* row_ptr(const char* base, int64_t row, int64_t row_bytes) {
+    return reinterpret_cast<const uint4*>(base + row * row_bytes);
+}
+
+template <typename T, int D, int GT, int NW, int TPL>
+__global__ __launch_bounds__(NW * kWave) void partial_kernel(PartialParams p) {
+    constexpr int E = Storage<T>::kElems;  // elements per 16-byte segment
+    constexpr int SEGS = D / E;            // lanes per row
+    constexpr int RG = kWave / SEGS;       // rows per wave-wide load
+    constexpr int BT = RG * TPL;           // tokens per wave block
+    static_assert(SEGS >= 8 && SEGS <= 32 && RG * SEGS == kWave, "row layout");
+
+    __shared__ float sm_acc[NW][GT][D];
+    __shared__ float sm_m[NW][GT];
+    __shared__ float sm_l[NW][GT];
+
+    const int chunk_idx = blockIdx.x;
+    const int h0 = blockIdx.y * GT;
+    const int b = blockIdx.z;
+    const int g = h0 / p.group;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int seg = lane % SEGS;
+    const int rg = lane / SEGS;
+
+    int n = p.seqlens ? p.seqlens[b] : p.N;
+    n = n < 0 ? 0 : (n > p.N ? p.N : n);
+    const int64_t c0 = (int64_t)chunk_idx * p.chunk;
+    const int64_t c1 = (c0 + p.chunk < (int64_t)n) ? c0 + p.chunk : (int64_t)n;
+
+    float* po = p.po + (int64_t)b * p.po_sb + (int64_t)h0 * p.po_sh + (int64_t)chunk_idx * p.po_sp;
+    float* pl = p.plse + (int64_t)b * p.pl_sb + (int64_t)h0 * p.pl_sh + (int64_t)chunk_idx * p.pl_sp;
+
+    if (c0 >= c1) {  // empty chunk: the identity state
+        for (int i = tid; i < GT * (D / 4); i += NW * kWave) {
+            const int h = i / (D / 4), c4 = i % (D / 4);
+            *reinterpret_cast<float4*>(po + (int64_t)h * p.po_sh + 4 * c4) = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c4 == 0) pl[(int64_t)h * p.pl_sh] = -INFINITY;
+        }
+        return;
+    }
+
+    // this lane's 16-byte segment of q for each head of the group
+    uint4 qs[GT];
+    {
+        const char* qb = reinterpret_cast<const char*>(p.q) + ((int64_t)b * p.q_sb + (int64_t)h0 * p.q_sh) * (int64_t)sizeof(T);
+#pragma unroll
+        for (int h = 0; h < GT; ++h)
+            qs[h] = *reinterpret_cast<const uint4*>(qb + (int64_t)h * p.q_sh * (int64_t)sizeof(T) + seg * 16);
+    }
+
+    const int64_t ks_bytes = p.k_st * (int64_t)sizeof(T);
+    const int64_t vs_bytes = p.v_st * (int64_t)sizeof(T);
+    const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.k_sb + (int64_t)g * p.k_sh) * (int64_t)sizeof(T) + seg * 16;
+    const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.v_sb + (int64_t)g * p.v_sh) * (int64_t)sizeof(T) + seg * 16;
+
+    float m[GT], l[GT], acc[GT][E];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = 0.0f;
+    }
+
+    const int64_t last = c1 - 1;
+    // rows past the chunk end are clamped to its last row (always valid memory) and masked
+    auto load_block = [&](int64_t t0, uint4 (&kb)[TPL], uint4 (&vb)[TPL]) {
+#pragma unroll
+        for (int j = 0; j < TPL; ++j) {
+            int64_t t = t0 + j * RG + rg;
+            t = t < last ? t : last;
+            kb[j] = *row_ptr(kbase, t, ks_bytes);
+            vb[j] = *row_ptr(vbase, t, vs_bytes);
+        }
+    };
+
+    auto compute_block = [&](int64_t t0, const uint4 (&kb)[TPL], const uint4 (&vb)[TPL]) {
+        float s[TPL][GT];
+#pragma unroll
+        for (int j = 0; j < TPL; ++j) {
+            const bool valid = t0 + j * RG + rg <= last;
+#pragma unroll
+            for (int h = 0; h < GT; ++h) {
+                const float dot = group_sum<SEGS>(seg_dot<T>(qs[h], kb[j]));
+                s[j][h] = valid ? dot * p.scale_log2 : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+            float bm = s[0][h];
+#pragma unroll
+            for (int j = 1; j < TPL; ++j) bm = fmaxf(bm, s[j][h]);
+            const float mn = fmaxf(m[h], bm);
+            const float ref = (mn == -INFINITY) ? 0.0f : mn;
+            const float alpha = exp2_fast(m[h] - ref);
+            float lsum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < TPL; ++j) {
+                s[j][h] = exp2_fast(s[j][h] - ref);
+                lsum += s[j][h];
+            }
+            l[h] = l[h] * alpha + lsum;
+            m[h] = mn;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+        }
+#pragma unroll
+        for (int j = 0; j < TPL; ++j) {
+            float vf[E];
+            seg_widen<T>(vb[j], vf);
+#pragma unroll
+            for (int h = 0; h < GT; ++h)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[h][e] = fmaf(s[j][h], vf[e], acc[h][e]);
+        }
+    };
+
+    const int64_t nblk = (c1 - c0 + BT - 1) / BT;
+    {
+        uint4 kA[TPL], vA[TPL], kB[TPL], vB[TPL];
+        int64_t blk = wave;
+        if (blk < nblk) load_block(c0 + blk * BT, kA, vA);
+        while (blk < nblk) {
+            int64_t nxt = blk + NW;
+            if (nxt < nblk) load_block(c0 + nxt * BT, kB, vB);
+            compute_block(c0 + blk * BT, kA, vA);
+            blk = nxt;
+            if (blk >= nblk) break;
+            nxt = blk + NW;
+            if (nxt < nblk) load_block(c0 + nxt * BT, kA, vA);
+            compute_block(c0 + blk * BT, kB, vB);
+            blk = nxt;
+        }
+    }
+
+    // merge the row groups of this wave (lanes that hold the same channels)
+#pragma unroll
+    for (int off = SEGS; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+            const float mo = __shfl_xor(m[h], off, kWave);
+            const float lo = __shfl_xor(l[h], off, kWave);
+            const Rescale r = merge_factors(m[h], mo);
+            l[h] = r.a * l[h] + r.b * lo;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float ao = __shfl_xor(acc[h][e], off, kWave);
+                acc[h][e] = r.a * acc[h][e] + r.b * ao;
+            }
+            m[h] = r.m;
+        }
+    }
+
+    // then the waves, through LDS
+    if (rg == 0) {
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) sm_acc[wave][h][seg * E + e] = acc[h][e];
+            if (seg == 0) {
+                sm_m[wave][h] = m[h];
+                sm_l[wave][h] = l[h];
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < GT * (D / 4); i += NW * kWave) {
+        const int h = i / (D / 4), c4 = i % (D / 4);
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+        const float ref = (M == -INFINITY) ? 0.0f : M;
+        float L = 0.0f;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = exp2_fast(sm_m[w][h] - ref);
+            L += f * sm_l[w][h];
+            o.x += f * sm_acc[w][h][4 * c4 + 0];
+            o.y += f * sm_acc[w][h][4 * c4 + 1];
+            o.z += f * sm_acc[w][h][4 * c4 + 2];
+            o.w += f * sm_acc[w][h][4 * c4 + 3];
+        }
+        float lse = -INFINITY;
+        if (L > 0.0f) {
+            const float inv = 1.0f / L;
+            o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+            lse = (M + __log2f(L)) * kLn2;
+        } else {
+            o = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        *reinterpret_cast<float4*>(po + (int64_t)h * p.po_sh + 4 * c4) = o;
+        if (c4 == 0) pl[(int64_t)h * p.pl_sh] = lse;
+    }
+}
+
+template <typename T, int D, int GT>
+hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hipStream_t stream) {
+    constexpr int NW = 4;
+    constexpr int TPL = GT >= 8 ? 4 : 8;
+    dim3 grid(n_chunks, Hq / GT, B);
+    hipLaunchKernelGGL((partial_kernel<T, D, GT, NW, TPL>), grid, dim3(NW * kWave), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_heads(const PartialParams& p, int gt, int B, int Hq, int n_chunks, hipStream_t stream) {
+    switch (gt) {
+        case 1: return launch_typed<T, D, 1>(p, B, Hq, n_chunks, stream);
+        case 2: return launch_typed<T, D, 2>(p, B, Hq, n_chunks, stream);
+        case 4: return launch_typed<T, D, 4>(p, B, Hq, n_chunks, stream);
+        case 8: return launch_typed<T, D, 8>(p, B, Hq, n_chunks, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_partial(const PartialParams& p, Dtype dt, int d, int heads_per_wg, int B, int Hq,
+                          int n_chunks, hipStream_t stream) {
+    if (dt == Dtype::BF16) {
+        if (d == 128) return launch_heads<uint16_t, 128>(p, heads_per_wg, B, Hq, n_chunks, stream);
+        if (d == 64) return launch_heads<uint16_t, 64>(p, heads_per_wg, B, Hq, n_chunks, stream);
+    } else {
+        if (d == 128) return launch_heads<float, 128>(p, heads_per_wg, B, Hq, n_chunks, stream);
+        if (d == 64) return launch_heads<float, 64>(p, heads_per_wg, B, Hq, n_chunks, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ta

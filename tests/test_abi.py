@@ -1,0 +1,156 @@
+"""Host-side checks of the C ABI: the library loads, exports what
+include/tree_attn.h declares, and rejects bad descriptors before touching the
+GPU (argument validation runs before any HIP call, so these need no device;
+the data pointers below are never dereferenced)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import softmax_tree_reduction_amd as ta
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a 16-byte aligned non-null address; validation never reads it
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ta.library_path()),
+                                reason="libtreeattn.so not built")
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names.update(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ta_\w+)\s*\(", src, flags=re.M))
+    return names
+
+
+def test_exports_every_declared_symbol():
+    lib = ta.load_library()
+    names = declared_functions()
+    assert {"ta_decode", "ta_combine", "ta_partial", "ta_last_error", "ta_version"} <= names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+    assert set(ta.EXPORTS) == names
+    assert lib.ta_version() == 1
+    assert lib.ta_last_error() is not None
+
+
+def T(shape, dtype=ta.TA_BF16, stride=None, data=FAKE):
+    if stride is None:
+        stride, acc = [], 1
+        for s in reversed(shape):
+            stride.insert(0, acc)
+            acc *= s
+    return ta.TaTensor.make(data, dtype, shape, stride)
+
+
+def good(B=2, Hq=8, Hkv=2, N=1000, d=128, dt=ta.TA_BF16):
+    return dict(q=T([B, Hq, d], dt), k=T([B, Hkv, N, d], dt), v=T([B, Hkv, N, d], dt),
+                out=T([B, Hq, d], ta.TA_F32), lse=T([B, Hq], ta.TA_F32))
+
+
+def call_decode(a, chunk=256):
+    lib = ta.load_library()
+    ref = lambda x: None if x is None else ctypes.byref(x)
+    rc = lib.ta_decode(ref(a["q"]), ref(a["k"]), ref(a["v"]), None, ref(a["out"]), ref(a.get("lse")), chunk, None)
+    return rc, lib.ta_last_error().decode()
+
+
+def call_partial(a, po, pl, chunk=256):
+    lib = ta.load_library()
+    rc = lib.ta_partial(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]), None,
+                        ctypes.byref(po), ctypes.byref(pl), chunk, None)
+    return rc, lib.ta_last_error().decode()
+
+
+def call_combine(po, pl, n, out, lse):
+    lib = ta.load_library()
+    ref = lambda x: None if x is None else ctypes.byref(x)
+    rc = lib.ta_combine(ref(po), ref(pl), n, ref(out), ref(lse), None)
+    return rc, lib.ta_last_error().decode()
+
+
+@pytest.mark.parametrize("mutate,code,needle", [
+    (lambda a: a.update(q=None), ta.TA_ERR_NULL, "q"),
+    (lambda a: a.update(out=None), ta.TA_ERR_NULL, "out"),
+    (lambda a: setattr(a["k"], "data", None), ta.TA_ERR_NULL, "k"),
+    (lambda a: setattr(a["q"], "ndim", 2), ta.TA_ERR_SHAPE, "dimensions"),
+    (lambda a: a.update(q=T([2, 6, 128])), ta.TA_ERR_SHAPE, "multiple"),     # 6 % 4 != 0 after k change below
+    (lambda a: a.update(v=T([2, 2, 999, 128])), ta.TA_ERR_SHAPE, "differ"),
+    (lambda a: a.update(k=T([3, 2, 1000, 128]), v=T([3, 2, 1000, 128])), ta.TA_ERR_SHAPE, "batch"),
+    (lambda a: a.update(v=T([2, 2, 1000, 128], ta.TA_F32)), ta.TA_ERR_DTYPE, "dtype"),
+    (lambda a: setattr(a["q"], "dtype", 7), ta.TA_ERR_DTYPE, "dtype"),
+    (lambda a: a.update(out=T([2, 8, 128], ta.TA_BF16)), ta.TA_ERR_DTYPE, "out"),
+    (lambda a: a.update(out=T([2, 8, 64], ta.TA_F32)), ta.TA_ERR_SHAPE, "out"),
+    (lambda a: a.update(lse=T([2, 4], ta.TA_F32)), ta.TA_ERR_SHAPE, "lse"),
+    (lambda a: a.update(k=T([2, 2, 1000, 128], stride=[256000, 128000, 128, 2])), ta.TA_ERR_STRIDE, "contiguous"),
+    (lambda a: a.update(k=T([2, 2, 1000, 128], stride=[257000, 128500, 129, 1])), ta.TA_ERR_STRIDE, "16 bytes"),
+    (lambda a: setattr(a["v"], "data", FAKE + 2), ta.TA_ERR_STRIDE, "aligned"),
+])
+def test_decode_validation(mutate, code, needle):
+    a = good()
+    if needle == "multiple":
+        a = good(Hq=8, Hkv=4)
+        a["q"] = T([2, 6, 128])
+        a["out"] = T([2, 6, 128], ta.TA_F32)
+        a["lse"] = T([2, 6], ta.TA_F32)
+        a["k"] = T([2, 4, 1000, 128])
+        a["v"] = T([2, 4, 1000, 128])
+    else:
+        mutate(a)
+    rc, msg = call_decode(a)
+    assert rc == code, msg
+    assert needle in msg
+
+
+def test_decode_unsupported_and_bad_chunk():
+    rc, msg = call_decode(good(d=96))
+    assert rc == ta.TA_ERR_UNSUPPORTED and "96" in msg
+    rc, msg = call_decode(good(), chunk=0)
+    assert rc == ta.TA_ERR_ARG and "chunk" in msg
+    rc, msg = call_decode(good(B=70000))
+    assert rc == ta.TA_ERR_UNSUPPORTED
+
+
+def test_decode_empty_batch_is_a_no_op():
+    # B = 0: valid, nothing to launch
+    rc, msg = call_decode(good(B=0))
+    assert rc == ta.TA_OK, msg
+
+
+def test_partial_validation():
+    a = good(N=1000)
+    # 1000 tokens in chunks of 256 need 4 partial states
+    rc, msg = call_partial(a, T([2, 8, 3, 128], ta.TA_F32), T([2, 8, 3], ta.TA_F32))
+    assert rc == ta.TA_ERR_SHAPE and "needs 4" in msg
+    rc, msg = call_partial(a, T([2, 8, 4, 128], ta.TA_BF16), T([2, 8, 4], ta.TA_F32))
+    assert rc == ta.TA_ERR_DTYPE
+    rc, msg = call_partial(a, T([2, 8, 4, 128], ta.TA_F32), T([2, 8, 5], ta.TA_F32))
+    assert rc == ta.TA_ERR_SHAPE
+
+
+def test_combine_validation():
+    po, pl = T([2, 8, 16, 128], ta.TA_F32), T([2, 8, 16], ta.TA_F32)
+    out, lse = T([2, 8, 128], ta.TA_F32), T([2, 8], ta.TA_F32)
+    assert call_combine(None, pl, 4, out, lse)[0] == ta.TA_ERR_NULL
+    assert call_combine(po, pl, 17, out, lse)[0] == ta.TA_ERR_ARG
+    assert call_combine(po, pl, -1, out, lse)[0] == ta.TA_ERR_ARG
+    assert call_combine(po, T([2, 8, 15], ta.TA_F32), 4, out, lse)[0] == ta.TA_ERR_SHAPE
+    assert call_combine(T([2, 8, 16, 96], ta.TA_F32), pl, 4, T([2, 8, 96], ta.TA_F32), lse)[0] == ta.TA_ERR_UNSUPPORTED
+    assert call_combine(po, pl, 4, T([2, 8, 64], ta.TA_F32), lse)[0] == ta.TA_ERR_SHAPE
+    assert call_combine(po, pl, 4, out, T([2, 8], ta.TA_BF16))[0] == ta.TA_ERR_DTYPE
+    rc, msg = call_combine(T([0, 8, 16, 128], ta.TA_F32), T([0, 8, 16], ta.TA_F32), 4,
+                           T([0, 8, 128], ta.TA_F32), T([0, 8], ta.TA_F32))
+    assert rc == ta.TA_OK, msg
+
+
+def test_last_error_is_per_call():
+    rc, msg = call_decode(good(), chunk=0)
+    assert rc != 0 and msg
+    rc, msg = call_decode(good(B=0))
+    assert rc == 0 and msg == ""
