@@ -94,6 +94,10 @@ def main() -> int:
     ap.add_argument("--min-rotation-bytes", type=float, default=2 * 2**30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--mode", choices=["step", "partial", "copy"], default="step",
+                    help="step: the benchmark line (default); partial: only the timed partial-kernel launches "
+                         "(for counter runs); copy: a plain device copy of --copy-mib MiB (counter calibration)")
+    ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -114,6 +118,17 @@ def main() -> int:
     chunk = args.chunk or wl.chunk
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.mode == "copy":
+        # a plain copy of known size: each launch reads and writes copy-mib MiB
+        n = args.copy_mib * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4,
+                          "launches": args.warmup + args.steps}))
+        return 0
     print(f"bench: generating {wl.name} (seed {args.seed})", file=sys.stderr, flush=True)
     inp = W.make_decode_inputs(wl, args.seed)
     step_bytes = algorithmic_bytes(wl, inp.seqlens)
@@ -134,6 +149,18 @@ def main() -> int:
         vs.append(v0.clone())
     print(f"bench: {copies} resident copies of the {cache_bytes / 2**20:.0f} MiB cache", file=sys.stderr, flush=True)
 
+    stream = torch.cuda.current_stream(dev)
+    P = -(-wl.N // chunk)
+    if args.mode == "partial":
+        po = torch.empty(wl.B, wl.Hq, P, wl.d, dtype=torch.float32, device=dev)
+        pl = torch.empty(wl.B, wl.Hq, P, dtype=torch.float32, device=dev)
+        for i in range(args.warmup + args.steps):
+            ta.partial(q, ks[i % copies], vs[i % copies], sl, chunk=chunk, partial_o=po, partial_lse=pl)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "partial", "workload": wl.name, "launches": args.warmup + args.steps,
+                          "algorithmic_bytes_per_launch": step_bytes - wl.B * wl.Hq * (wl.d + 1) * 4}))
+        return 0
+
     # parity of this launch configuration on sampled rows before timing
     import oracle
     out, lse = ta.decode(q, k0, v0, sl, chunk=chunk)
@@ -150,9 +177,6 @@ def main() -> int:
         return 1
     print(f"bench: parity on {len(rows)} sampled rows ok (max|out-oracle| {perr:.2e}, lse rel {lerr:.2e})",
           file=sys.stderr, flush=True)
-
-    stream = torch.cuda.current_stream(dev)
-    P = -(-wl.N // chunk)
 
     # ---- whole step: ta_decode (partial kernel + tree merge)
     for i in range(args.warmup):
