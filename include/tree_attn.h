@@ -92,9 +92,13 @@ enum {
  *   chunk    tokens per partial state, >= 1
  *
  * Supported: d in {64, 128}; Hq a multiple of Hkv; B <= 65535; Hq <= 65535.
- * Needs Hq * P * (d + 1) * 4 bytes of stream-ordered device workspace per
- * sequence (P = ceil(N / chunk)), allocated and released on `stream` by the
- * library (hipMallocAsync / hipFreeAsync).
+ * Needs Hq * P * (d + 1) * 4 bytes of device workspace per sequence
+ * (P = ceil(N / chunk)). The library keeps one workspace buffer per (device,
+ * stream), allocated with hipMallocAsync on that stream the first time it is
+ * needed and grown when a call needs more; it is held until the process ends.
+ * Calls on one stream run in stream order and so never share it concurrently.
+ * While the stream is being captured into a graph the workspace is allocated
+ * and released inside the captured work instead.
  */
 int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v,
               const int32_t* seqlens, const ta_tensor* out, const ta_tensor* lse,
@@ -115,7 +119,7 @@ int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v,
  * i + 2^t for every i that is a multiple of 2^(t+1) (a node without a partner
  * passes up unchanged), giving ceil(log2 n_parts) levels.
  * Supported: d in {64, 128}. n_parts above 128 (d = 128) or 256 (d = 64) runs
- * the same tree in several launches and takes stream-ordered workspace.
+ * the same tree in several launches and takes workspace as ta_decode does.
  */
 int ta_combine(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts,
                const ta_tensor* out, const ta_tensor* lse, void* stream);

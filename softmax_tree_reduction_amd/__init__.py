@@ -84,38 +84,58 @@ def _check(rc: int) -> None:
 
 
 # ----------------------------------------------------------------------------
-# torch glue (imported lazily so the CPU-side ABI tests need no GPU)
+# torch glue (imported lazily so the CPU-side ABI tests need no GPU). The calls
+# below run once per decode step, so they keep the Python work per call small.
 # ----------------------------------------------------------------------------
 
-def _desc(t) -> TaTensor:
-    import torch
-    if t.dtype == torch.float32:
-        dt = TA_F32
-    elif t.dtype == torch.bfloat16:
-        dt = TA_BF16
-    else:
+_DTYPES = None
+
+
+def _dtype_code(t) -> int:
+    global _DTYPES
+    if _DTYPES is None:
+        import torch
+        _DTYPES = {torch.float32: TA_F32, torch.bfloat16: TA_BF16}
+    dt = _DTYPES.get(t.dtype)
+    if dt is None:
         raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+    return dt
+
+
+def _desc(t) -> TaTensor:
     if not t.is_cuda:
         raise ValueError("tensors must live on the GPU")
-    return TaTensor.make(t.data_ptr(), dt, t.shape, t.stride())
+    d = TaTensor()
+    d.data = t.data_ptr()
+    d.dtype = _dtype_code(t)
+    shape, stride = t.shape, t.stride()
+    n = len(shape)
+    d.ndim = n
+    d.shape[0:n] = shape
+    d.stride[0:n] = stride
+    return d
 
 
-def _stream_handle(stream, device):
+def _call(dev, stream, fn):
+    """Run fn(stream_handle) with `dev` current."""
     import torch
+    if torch.cuda.current_device() != dev.index:
+        with torch.cuda.device(dev):
+            return _call(dev, stream, fn)
     if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
+        stream = torch.cuda.current_stream(dev)
+    _check(fn(ctypes.c_void_p(stream.cuda_stream)))
 
 
 def _seqlens_ptr(seqlens, B, device):
     import torch
     if seqlens is None:
-        return None, None
+        return None
     if not (seqlens.is_cuda and seqlens.dtype == torch.int32 and seqlens.is_contiguous() and seqlens.numel() == B):
         raise ValueError("seqlens must be a contiguous int32 CUDA tensor with one entry per sequence")
     if seqlens.device != device:
         raise ValueError("seqlens must be on the same device as q")
-    return ctypes.c_void_p(seqlens.data_ptr()), seqlens
+    return ctypes.c_void_p(seqlens.data_ptr())
 
 
 def _same_device(*ts):
@@ -135,13 +155,11 @@ def decode(q, k, v, seqlens=None, chunk: int = 2048, out=None, lse=None, stream=
         out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
-    sl, _keep = _seqlens_ptr(seqlens, B, dev)
-    lib = load_library()
-    with torch.cuda.device(dev):
-        args = [_desc(q), _desc(k), _desc(v)]
-        o_d, l_d = _desc(out), _desc(lse)
-        _check(lib.ta_decode(*[ctypes.byref(a) for a in args], sl, ctypes.byref(o_d), ctypes.byref(l_d),
-                             int(chunk), _stream_handle(stream, dev)))
+    sl = _seqlens_ptr(seqlens, B, dev)
+    lib = _lib or load_library()
+    dq, dk, dv, do, dl = _desc(q), _desc(k), _desc(v), _desc(out), _desc(lse)
+    by = ctypes.byref
+    _call(dev, stream, lambda s: lib.ta_decode(by(dq), by(dk), by(dv), sl, by(do), by(dl), int(chunk), s))
     return out, lse
 
 
@@ -156,13 +174,11 @@ def partial(q, k, v, seqlens=None, chunk: int = 2048, partial_o=None, partial_ls
         partial_o = torch.empty(B, Hq, P, d, dtype=torch.float32, device=dev)
     if partial_lse is None:
         partial_lse = torch.empty(B, Hq, P, dtype=torch.float32, device=dev)
-    sl, _keep = _seqlens_ptr(seqlens, B, dev)
-    lib = load_library()
-    with torch.cuda.device(dev):
-        args = [_desc(q), _desc(k), _desc(v)]
-        po_d, pl_d = _desc(partial_o), _desc(partial_lse)
-        _check(lib.ta_partial(*[ctypes.byref(a) for a in args], sl, ctypes.byref(po_d), ctypes.byref(pl_d),
-                              int(chunk), _stream_handle(stream, dev)))
+    sl = _seqlens_ptr(seqlens, B, dev)
+    lib = _lib or load_library()
+    dq, dk, dv, dpo, dpl = _desc(q), _desc(k), _desc(v), _desc(partial_o), _desc(partial_lse)
+    by = ctypes.byref
+    _call(dev, stream, lambda s: lib.ta_partial(by(dq), by(dk), by(dv), sl, by(dpo), by(dpl), int(chunk), s))
     return partial_o, partial_lse
 
 
@@ -177,9 +193,8 @@ def combine(partial_o, partial_lse, n_parts=None, out=None, lse=None, stream=Non
         out = torch.empty(B, H, d, dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty(B, H, dtype=torch.float32, device=dev)
-    lib = load_library()
-    with torch.cuda.device(dev):
-        po_d, pl_d, o_d, l_d = _desc(partial_o), _desc(partial_lse), _desc(out), _desc(lse)
-        _check(lib.ta_combine(ctypes.byref(po_d), ctypes.byref(pl_d), int(n_parts), ctypes.byref(o_d),
-                              ctypes.byref(l_d), _stream_handle(stream, dev)))
+    lib = _lib or load_library()
+    dpo, dpl, do, dl = _desc(partial_o), _desc(partial_lse), _desc(out), _desc(lse)
+    by = ctypes.byref
+    _call(dev, stream, lambda s: lib.ta_combine(by(dpo), by(dpl), int(n_parts), by(do), by(dl), s))
     return out, lse

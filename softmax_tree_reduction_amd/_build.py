@@ -28,10 +28,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile every source, link the shared library in place, return its path."""
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str = LIB,
+          objdir: str | None = None) -> str:
+    """Compile every source, link the shared library (in place by default), return its path."""
     cc = hipcc()
-    objdir = os.path.join(HERE, "_build")
+    objdir = objdir or os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     flags = HIP_FLAGS + list(extra_flags or [])
 
@@ -45,13 +46,13 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
 
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + f".tmp{os.getpid()}"
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <map>
 #include <mutex>
 #include <string>
 
@@ -75,6 +76,75 @@ void keep_pool_cached(int device) {
         (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
     }
     done[device] = true;
+}
+
+// Device scratch of one call, ordered on the call's stream. Outside graph capture
+// it is a buffer kept per (device, stream) and grown when a call needs more, so a
+// steady decode loop allocates nothing; work on one stream runs in order, so calls
+// on the same stream never overlap in it. Under graph capture the scratch is
+// allocated and released inside the captured work instead.
+class CallWorkspace {
+  public:
+    explicit CallWorkspace(hipStream_t st) : st_(st) {}
+    ~CallWorkspace() {
+        if (owned_ && ptr_) (void)hipFreeAsync(ptr_, st_);
+    }
+    CallWorkspace(const CallWorkspace&) = delete;
+    CallWorkspace& operator=(const CallWorkspace&) = delete;
+
+    int acquire(size_t bytes) {
+        if (bytes == 0) return TA_OK;
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        keep_pool_cached(dev);
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if ((e = hipStreamIsCapturing(st_, &cap)) != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+        if (cap != hipStreamCaptureStatusNone) {
+            if ((e = hipMallocAsync(&ptr_, bytes, st_)) != hipSuccess) return hip_fail(e, "hipMallocAsync (workspace)");
+            owned_ = true;
+            return TA_OK;
+        }
+        std::lock_guard<std::mutex> lock(cache_mu());
+        Entry& w = cache()[{dev, reinterpret_cast<uintptr_t>(st_)}];
+        if (w.bytes < bytes) {
+            const size_t nb = bytes > w.bytes + w.bytes / 2 ? bytes : w.bytes + w.bytes / 2;
+            void* p = nullptr;
+            if ((e = hipMallocAsync(&p, nb, st_)) != hipSuccess) return hip_fail(e, "hipMallocAsync (workspace)");
+            if (w.ptr) (void)hipFreeAsync(w.ptr, st_);
+            w.ptr = p;
+            w.bytes = nb;
+        }
+        ptr_ = w.ptr;
+        return TA_OK;
+    }
+    void* get() const { return ptr_; }
+
+  private:
+    struct Entry {
+        void* ptr = nullptr;
+        size_t bytes = 0;
+    };
+    static std::mutex& cache_mu() {
+        static std::mutex mu;
+        return mu;
+    }
+    static std::map<std::pair<int, uintptr_t>, Entry>& cache() {
+        static auto* m = new std::map<std::pair<int, uintptr_t>, Entry>();  // lives until exit
+        return *m;
+    }
+    hipStream_t st_;
+    void* ptr_ = nullptr;
+    bool owned_ = false;
+};
+
+// Bytes of intermediate states the merge needs when a row has more leaves than one
+// workgroup takes: two buffers of the first pass's output size.
+size_t combine_scratch_bytes(int64_t n_parts, int64_t B, int64_t H, int64_t d) {
+    const int64_t span = ta::combine_max_leaves((int)d);
+    if (n_parts <= span) return 0;
+    const int64_t groups = (n_parts + span - 1) / span;
+    return 2 * (size_t)(B * H * groups * (d + 1)) * sizeof(float);
 }
 
 struct DecodeShape {
@@ -180,10 +250,10 @@ ta::PartialParams partial_params(const ta_tensor* q, const ta_tensor* k, const t
 
 // Runs the merge tree over n_parts leaves per row and writes (out, lse).
 // Rows with more leaves than one workgroup takes go through intermediate levels
-// held in stream-ordered workspace.
+// held in `scratch` (combine_scratch_bytes of it).
 int run_combine(const float* po, const int64_t po_st[3], const float* pl, const int64_t pl_st[3], int64_t n_parts,
                 const int32_t* seqlens, int32_t chunk, int64_t N, int64_t B, int64_t H, int64_t d, float* out,
-                const int64_t out_st[2], float* lse, const int64_t lse_st[2], hipStream_t stream) {
+                const int64_t out_st[2], float* lse, const int64_t lse_st[2], void* scratch, hipStream_t stream) {
     const int64_t span = ta::combine_max_leaves((int)d);
     const float* cur_o = po;
     const float* cur_l = pl;
@@ -191,23 +261,15 @@ int run_combine(const float* po, const int64_t po_st[3], const float* pl, const 
     int64_t cur_pl[3] = {pl_st[0], pl_st[1], pl_st[2]};
     int64_t leaves = n_parts;
     const int32_t* sl = seqlens;
-    void* scratch[2] = {nullptr, nullptr};
+    const int64_t first_groups = (n_parts + span - 1) / span;
+    float* bufs[2] = {static_cast<float*>(scratch), nullptr};
+    if (scratch) bufs[1] = bufs[0] + B * H * first_groups * (d + 1);
     int which = 0;
-    int rc = TA_OK;
     hipError_t e = hipSuccess;
 
     while (leaves > span) {
         const int64_t groups = (leaves + span - 1) / span;
-        const size_t bytes = (size_t)(B * H * groups * (d + 1)) * sizeof(float);
-        if (scratch[which]) {
-            (void)hipFreeAsync(scratch[which], stream);
-            scratch[which] = nullptr;
-        }
-        if ((e = hipMallocAsync(&scratch[which], bytes, stream)) != hipSuccess) {
-            rc = hip_fail(e, "hipMallocAsync (merge workspace)");
-            break;
-        }
-        float* nxt_o = static_cast<float*>(scratch[which]);
+        float* nxt_o = bufs[which];
         float* nxt_l = nxt_o + B * H * groups * d;
         ta::CombineParams c{};
         c.po = cur_o;
@@ -222,10 +284,8 @@ int run_combine(const float* po, const int64_t po_st[3], const float* pl, const 
         c.lse = nxt_l;
         c.out_sb = H * groups * d; c.out_sh = groups * d; c.out_sg = d;
         c.lse_sb = H * groups; c.lse_sh = groups; c.lse_sg = 1;
-        if ((e = ta::launch_combine_pass(c, (int)d, (int)B, (int)H, (int)groups, (int)span, stream)) != hipSuccess) {
-            rc = hip_fail(e, "merge kernel launch");
-            break;
-        }
+        if ((e = ta::launch_combine_pass(c, (int)d, (int)B, (int)H, (int)groups, (int)span, stream)) != hipSuccess)
+            return hip_fail(e, "merge kernel launch");
         cur_o = nxt_o;
         cur_l = nxt_l;
         cur_po[0] = c.out_sb; cur_po[1] = c.out_sh; cur_po[2] = c.out_sg;
@@ -234,26 +294,22 @@ int run_combine(const float* po, const int64_t po_st[3], const float* pl, const 
         sl = nullptr;  // empty groups were written as empty states
         which ^= 1;
     }
-    if (rc == TA_OK) {
-        ta::CombineParams c{};
-        c.po = cur_o;
-        c.plse = cur_l;
-        c.po_sb = cur_po[0]; c.po_sh = cur_po[1]; c.po_sp = cur_po[2];
-        c.pl_sb = cur_pl[0]; c.pl_sh = cur_pl[1]; c.pl_sp = cur_pl[2];
-        c.n_parts = (int32_t)leaves;
-        c.seqlens = sl;
-        c.chunk = chunk;
-        c.N = (int32_t)N;
-        c.out = out;
-        c.lse = lse;
-        c.out_sb = out_st[0]; c.out_sh = out_st[1]; c.out_sg = 0;
-        c.lse_sb = lse ? lse_st[0] : 0; c.lse_sh = lse ? lse_st[1] : 0; c.lse_sg = 0;
-        if ((e = ta::launch_combine_pass(c, (int)d, (int)B, (int)H, 1, (int)(leaves > 0 ? leaves : 1), stream)) != hipSuccess)
-            rc = hip_fail(e, "merge kernel launch");
-    }
-    for (void* s : scratch)
-        if (s) (void)hipFreeAsync(s, stream);
-    return rc;
+    ta::CombineParams c{};
+    c.po = cur_o;
+    c.plse = cur_l;
+    c.po_sb = cur_po[0]; c.po_sh = cur_po[1]; c.po_sp = cur_po[2];
+    c.pl_sb = cur_pl[0]; c.pl_sh = cur_pl[1]; c.pl_sp = cur_pl[2];
+    c.n_parts = (int32_t)leaves;
+    c.seqlens = sl;
+    c.chunk = chunk;
+    c.N = (int32_t)N;
+    c.out = out;
+    c.lse = lse;
+    c.out_sb = out_st[0]; c.out_sh = out_st[1]; c.out_sg = 0;
+    c.lse_sb = lse ? lse_st[0] : 0; c.lse_sh = lse ? lse_st[1] : 0; c.lse_sg = 0;
+    if ((e = ta::launch_combine_pass(c, (int)d, (int)B, (int)H, 1, (int)(leaves > 0 ? leaves : 1), stream)) != hipSuccess)
+        return hip_fail(e, "merge kernel launch");
+    return TA_OK;
 }
 
 }  // namespace
@@ -289,28 +345,23 @@ int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const 
     if (s.B == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t P = s.N > 0 ? (s.N + chunk - 1) / chunk : 1;  // N = 0: one empty state per row
-    const size_t bytes = (size_t)(s.B * s.Hq * P * (s.d + 1)) * sizeof(float);
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    keep_pool_cached(dev);
-    void* ws = nullptr;
-    if ((e = hipMallocAsync(&ws, bytes, st)) != hipSuccess) return hip_fail(e, "hipMallocAsync (partial states)");
-    float* po = static_cast<float*>(ws);
+    const size_t part_bytes = (size_t)(s.B * s.Hq * P * (s.d + 1)) * sizeof(float);
+    const size_t merge_bytes = combine_scratch_bytes(P, s.B, s.Hq, s.d);
+    CallWorkspace ws(st);
+    if ((rc = ws.acquire(part_bytes + merge_bytes)) != TA_OK) return rc;
+    float* po = static_cast<float*>(ws.get());
     float* pl = po + s.B * s.Hq * P * s.d;
+    void* merge_scratch = merge_bytes ? static_cast<char*>(ws.get()) + part_bytes : nullptr;
     const int64_t po_st[3] = {s.Hq * P * s.d, P * s.d, s.d};
     const int64_t pl_st[3] = {s.Hq * P, P, 1};
     const int gt = heads_per_wg(s.Hq / s.Hkv);
     ta::PartialParams p = partial_params(q, k, v, seqlens, po, po_st, pl, pl_st, s, chunk);
-    if ((e = ta::launch_partial(p, s.dt, (int)s.d, gt, (int)s.B, (int)s.Hq, (int)P, st)) != hipSuccess) {
-        (void)hipFreeAsync(ws, st);
-        return hip_fail(e, "partial kernel launch");
-    }
+    hipError_t e = ta::launch_partial(p, s.dt, (int)s.d, gt, (int)s.B, (int)s.Hq, (int)P, st);
+    if (e != hipSuccess) return hip_fail(e, "partial kernel launch");
     const int64_t out_st[2] = {out->stride[0], out->stride[1]};
     const int64_t lse_st[2] = {lse ? lse->stride[0] : 0, lse ? lse->stride[1] : 0};
     rc = run_combine(po, po_st, pl, pl_st, P, seqlens, chunk, s.N, s.B, s.Hq, s.d, static_cast<float*>(out->data),
-                     out_st, lse ? static_cast<float*>(lse->data) : nullptr, lse_st, st);
-    (void)hipFreeAsync(ws, st);
+                     out_st, lse ? static_cast<float*>(lse->data) : nullptr, lse_st, merge_scratch, st);
     if (rc != TA_OK) return rc;
     return ok();
 }
@@ -329,17 +380,14 @@ int ta_combine(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t
     if (B > 65535) return fail(TA_ERR_UNSUPPORTED, "batch %lld exceeds 65535", (long long)B);
     if (B == 0 || H == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (n_parts > ta::combine_max_leaves((int)d)) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-        keep_pool_cached(dev);
-    }
+    CallWorkspace ws(st);
+    if ((rc = ws.acquire(combine_scratch_bytes(n_parts, B, H, d))) != TA_OK) return rc;
     const int64_t out_st[2] = {out->stride[0], out->stride[1]};
     const int64_t lse_st[2] = {lse ? lse->stride[0] : 0, lse ? lse->stride[1] : 0};
     rc = run_combine(static_cast<const float*>(partial_o->data), partial_o->stride,
                      static_cast<const float*>(partial_lse->data), partial_lse->stride, n_parts, nullptr, 1, 0, B, H, d,
-                     static_cast<float*>(out->data), out_st, lse ? static_cast<float*>(lse->data) : nullptr, lse_st, st);
+                     static_cast<float*>(out->data), out_st, lse ? static_cast<float*>(lse->data) : nullptr, lse_st,
+                     ws.get(), st);
     if (rc != TA_OK) return rc;
     return ok();
 }

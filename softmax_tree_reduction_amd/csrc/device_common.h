@@ -4,6 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#ifndef TA_STREAM_NT
+#define TA_STREAM_NT 1
+#endif
+
 namespace ta {
 
 constexpr int kWave = 64;
@@ -13,6 +17,18 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Exact widening of a packed pair of bfloat16 values (low half = first element).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Streaming 16-byte load: each K/V byte is read once, so the load carries the
+// nontemporal hint and does not displace reusable lines from the caches.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+#if TA_STREAM_NT
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+#else
+    return *p;
+#endif
+}
 
 // 2^x on the hardware exponential unit; 2^-inf = 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

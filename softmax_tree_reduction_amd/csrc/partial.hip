@@ -28,6 +28,17 @@
 #include "device_common.h"
 #include "kernels.h"
 
+// Launch shape: waves per workgroup, tokens per lane per block, blocks in the register ring.
+#ifndef TA_PARTIAL_WAVES
+#define TA_PARTIAL_WAVES 4
+#endif
+#ifndef TA_PARTIAL_TPL
+#define TA_PARTIAL_TPL 4
+#endif
+#ifndef TA_PARTIAL_NBUF
+#define TA_PARTIAL_NBUF 2
+#endif
+
 namespace ta {
 namespace {
 
@@ -89,8 +100,11 @@ __device__ __forceinline__ const uint4* row_ptr(const char* base, int64_t row, i
     return reinterpret_cast<const uint4*>(base + row * row_bytes);
 }
 
-template <typename T, int D, int GT, int NW, int TPL>
-__global__ __launch_bounds__(NW * kWave) void partial_kernel(PartialParams p) {
+// The partial state of tokens [c0, c1) (c0 < c1) for the GT heads from h0, written to
+// po / pl (already offset to this sequence, head h0 and chunk).
+template <typename T, int D, int GT, int NW, int TPL, int NBUF>
+__device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h0, int g, int64_t c0, int64_t c1,
+                                            float* po, float* pl) {
     constexpr int E = Storage<T>::kElems;  // elements per 16-byte segment
     constexpr int SEGS = D / E;            // lanes per row
     constexpr int RG = kWave / SEGS;       // rows per wave-wide load
@@ -101,32 +115,11 @@ __global__ __launch_bounds__(NW * kWave) void partial_kernel(PartialParams p) {
     __shared__ float sm_m[NW][GT];
     __shared__ float sm_l[NW][GT];
 
-    const int chunk_idx = blockIdx.x;
-    const int h0 = blockIdx.y * GT;
-    const int b = blockIdx.z;
-    const int g = h0 / p.group;
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
     const int seg = lane % SEGS;
     const int rg = lane / SEGS;
-
-    int n = p.seqlens ? p.seqlens[b] : p.N;
-    n = n < 0 ? 0 : (n > p.N ? p.N : n);
-    const int64_t c0 = (int64_t)chunk_idx * p.chunk;
-    const int64_t c1 = (c0 + p.chunk < (int64_t)n) ? c0 + p.chunk : (int64_t)n;
-
-    float* po = p.po + (int64_t)b * p.po_sb + (int64_t)h0 * p.po_sh + (int64_t)chunk_idx * p.po_sp;
-    float* pl = p.plse + (int64_t)b * p.pl_sb + (int64_t)h0 * p.pl_sh + (int64_t)chunk_idx * p.pl_sp;
-
-    if (c0 >= c1) {  // empty chunk: the identity state
-        for (int i = tid; i < GT * (D / 4); i += NW * kWave) {
-            const int h = i / (D / 4), c4 = i % (D / 4);
-            *reinterpret_cast<float4*>(po + (int64_t)h * p.po_sh + 4 * c4) = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (c4 == 0) pl[(int64_t)h * p.pl_sh] = -INFINITY;
-        }
-        return;
-    }
 
     // this lane's 16-byte segment of q for each head of the group
     uint4 qs[GT];
@@ -158,8 +151,8 @@ __global__ __launch_bounds__(NW * kWave) void partial_kernel(PartialParams p) {
         for (int j = 0; j < TPL; ++j) {
             int64_t t = t0 + j * RG + rg;
             t = t < last ? t : last;
-            kb[j] = *row_ptr(kbase, t, ks_bytes);
-            vb[j] = *row_ptr(vbase, t, vs_bytes);
+            kb[j] = load_stream(row_ptr(kbase, t, ks_bytes));
+            vb[j] = load_stream(row_ptr(vbase, t, vs_bytes));
         }
     };
 
@@ -204,21 +197,27 @@ __global__ __launch_bounds__(NW * kWave) void partial_kernel(PartialParams p) {
         }
     };
 
+    // Ring of NBUF register buffers: blocks blk+NW, ..., blk+(NBUF-1)NW are in flight
+    // while block blk is computed.
     const int64_t nblk = (c1 - c0 + BT - 1) / BT;
     {
-        uint4 kA[TPL], vA[TPL], kB[TPL], vB[TPL];
+        uint4 kb[NBUF][TPL], vb[NBUF][TPL];
         int64_t blk = wave;
-        if (blk < nblk) load_block(c0 + blk * BT, kA, vA);
-        while (blk < nblk) {
-            int64_t nxt = blk + NW;
-            if (nxt < nblk) load_block(c0 + nxt * BT, kB, vB);
-            compute_block(c0 + blk * BT, kA, vA);
-            blk = nxt;
-            if (blk >= nblk) break;
-            nxt = blk + NW;
-            if (nxt < nblk) load_block(c0 + nxt * BT, kA, vA);
-            compute_block(c0 + blk * BT, kB, vB);
-            blk = nxt;
+#pragma unroll
+        for (int s = 0; s < NBUF - 1; ++s)
+            if (blk + s * NW < nblk) load_block(c0 + (blk + s * NW) * BT, kb[s], vb[s]);
+        bool more = blk < nblk;
+        while (more) {
+#pragma unroll
+            for (int s = 0; s < NBUF; ++s) {
+                if (more) {
+                    const int64_t pre = blk + (NBUF - 1) * NW;
+                    if (pre < nblk) load_block(c0 + pre * BT, kb[(s + NBUF - 1) % NBUF], vb[(s + NBUF - 1) % NBUF]);
+                    compute_block(c0 + blk * BT, kb[s], vb[s]);
+                    blk += NW;
+                    more = blk < nblk;
+                }
+            }
         }
     }
 
@@ -283,12 +282,41 @@ __global__ __launch_bounds__(NW * kWave) void partial_kernel(PartialParams p) {
     }
 }
 
+template <typename T, int D, int GT, int NW, int TPL, int NBUF>
+__global__ __launch_bounds__(NW * kWave) void partial_kernel(PartialParams p) {
+    const int chunk_idx = blockIdx.x;
+    const int h0 = blockIdx.y * GT;
+    const int b = blockIdx.z;
+    const int g = h0 / p.group;
+    const int tid = threadIdx.x;
+
+    int n = p.seqlens ? p.seqlens[b] : p.N;
+    n = n < 0 ? 0 : (n > p.N ? p.N : n);
+    const int64_t c0 = (int64_t)chunk_idx * p.chunk;
+    const int64_t c1 = (c0 + p.chunk < (int64_t)n) ? c0 + p.chunk : (int64_t)n;
+
+    float* po = p.po + (int64_t)b * p.po_sb + (int64_t)h0 * p.po_sh + (int64_t)chunk_idx * p.po_sp;
+    float* pl = p.plse + (int64_t)b * p.pl_sb + (int64_t)h0 * p.pl_sh + (int64_t)chunk_idx * p.pl_sp;
+
+    if (c0 >= c1) {  // empty chunk: the identity state
+        for (int i = tid; i < GT * (D / 4); i += NW * kWave) {
+            const int h = i / (D / 4), c4 = i % (D / 4);
+            *reinterpret_cast<float4*>(po + (int64_t)h * p.po_sh + 4 * c4) = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c4 == 0) pl[(int64_t)h * p.pl_sh] = -INFINITY;
+        }
+        return;
+    }
+    chunk_state<T, D, GT, NW, TPL, NBUF>(p, b, h0, g, c0, c1, po, pl);
+}
+
+
 template <typename T, int D, int GT>
 hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hipStream_t stream) {
-    constexpr int NW = 4;
-    constexpr int TPL = GT >= 8 ? 4 : 8;
+    constexpr int NW = TA_PARTIAL_WAVES;
+    constexpr int TPL = GT >= 8 ? (TA_PARTIAL_TPL > 4 ? 4 : TA_PARTIAL_TPL) : TA_PARTIAL_TPL;
     dim3 grid(n_chunks, Hq / GT, B);
-    hipLaunchKernelGGL((partial_kernel<T, D, GT, NW, TPL>), grid, dim3(NW * kWave), 0, stream, p);
+    constexpr int NBUF = TA_PARTIAL_NBUF;
+    hipLaunchKernelGGL((partial_kernel<T, D, GT, NW, TPL, NBUF>), grid, dim3(NW * kWave), 0, stream, p);
     return hipGetLastError();
 }
 

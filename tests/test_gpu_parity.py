@@ -175,3 +175,49 @@ def test_workload_sized_sampled_rows(name, n_rows):
     log(f"workload {name}: max abs out err {err:.2e}, max rel lse err {lerr:.2e}")
     # every row, sampled or not, is finite
     assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def _merged_by_separate_pass(q, k, v, sl, chunk):
+    po, pl = ta.partial(q, k, v, sl, chunk=chunk)
+    return ta.combine(po, pl)
+
+
+@pytest.mark.parametrize("N,chunk", [(2000, 300), (8000, 100), (8000, 63), (3000, 1)])
+def test_decode_equals_combine_of_partials(N, chunk):
+    # P = 7, 80 and 127 merge in one pass; P = 3000 in several passes
+    inp = W.random_decode(B=3, Hq=8, Hkv=2, N=N, d=128, dtype="bf16", seed=N + chunk,
+                          seqlens=[N, N // 3, 0])
+    q, k, v, sl = upload(inp)
+    log(f"decode vs partial + combine: N={N} chunk={chunk}")
+    for _ in range(3):  # repeated launches reuse the stream's workspace
+        out, lse = ta.decode(q, k, v, sl, chunk=chunk)
+        ref_o, ref_l = _merged_by_separate_pass(q, k, v, sl, chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+    ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", what=f"N={N} chunk={chunk}")
+
+
+def test_shapes_alternate_on_one_stream_and_a_second_stream():
+    # different head-group counts and partial counts reuse one stream's workspace; a
+    # second stream gets its own
+    cases = [W.random_decode(B=2, Hq=32, Hkv=8, N=5000, d=128, dtype="bf16", seed=s, seqlens=[5000, 77])
+             for s in (1, 2)] + [W.random_decode(B=5, Hq=4, Hkv=4, N=900, d=64, dtype="f32", seed=3,
+                                                  seqlens=[900, 1, 450, 0, 899])]
+    side = torch.cuda.Stream()
+    for rep in range(2):
+        for i, inp in enumerate(cases):
+            q, k, v, sl = upload(inp)
+            chunk = [256, 1024, 64][i]
+            stream = side if rep == 1 else None
+            if stream is not None:
+                stream.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(stream):
+                    out, lse = ta.decode(q, k, v, sl, chunk=chunk)
+                torch.cuda.current_stream().wait_stream(stream)
+            else:
+                out, lse = ta.decode(q, k, v, sl, chunk=chunk)
+            torch.cuda.synchronize()
+            ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+            dtype = "bf16" if inp.q.dtype == np.uint16 else "f32"
+            assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, dtype, what=f"case {i} rep {rep}")
