@@ -177,6 +177,10 @@ int check_decode_inputs(const ta_tensor* q, const ta_tensor* k, const ta_tensor*
     if (s->B > 65535) return fail(TA_ERR_UNSUPPORTED, "batch %lld exceeds 65535", (long long)s->B);
     if (s->Hq > 65535) return fail(TA_ERR_UNSUPPORTED, "query heads %lld exceed 65535", (long long)s->Hq);
     if (s->N > INT32_MAX - chunk) return fail(TA_ERR_UNSUPPORTED, "cache length %lld too large", (long long)s->N);
+    // the kernel addresses a row group's rows with 32-bit offsets from a shared base
+    const int64_t es = elem_size(q->dtype);
+    if (k->stride[2] * es >= (int64_t)1 << 28 || v->stride[2] * es >= (int64_t)1 << 28)
+        return fail(TA_ERR_UNSUPPORTED, "token stride of k or v is 256 MiB or more");
     return TA_OK;
 }
 

@@ -46,19 +46,80 @@ __device__ __forceinline__ float dpp_mov(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
 }
 
-// Sum over aligned groups of L consecutive lanes (L in {8, 16, 32}); every lane
-// of the group receives the group total. The pairings xor1, xor2, half-mirror,
-// mirror each join two disjoint halves of a growing aligned group, so after
-// log2(L) steps each lane holds the sum over its whole group.
-template <int L>
-__device__ __forceinline__ float group_sum(float x) {
-    static_assert(L == 8 || L == 16 || L == 32, "group size");
-    x += dpp_mov<kDppXor1>(x);
-    x += dpp_mov<kDppXor2>(x);
-    x += dpp_mov<kDppHalfMirror>(x);
-    if constexpr (L >= 16) x += dpp_mov<kDppMirror>(x);
-    if constexpr (L >= 32) x += __shfl_xor(x, 16, kWave);
-    return x;
+// The value of lane (this lane XOR K). K = 1, 2: quad permutes; K = 4: row_ror:N
+// gives lane i the value of lane (i - N) mod 16, so lanes whose bit 2 is clear read
+// lane i + 4 through row_ror:12 and the others lane i - 4 through row_ror:4, each
+// half written under its bank mask (a bank is 4 lanes); K = 8: row_ror:8 inside
+// the 16-lane row; K = 16: across rows through ds_bpermute.
+template <int K>
+__device__ __forceinline__ float lane_xor(float x) {
+    if constexpr (K == 1) {
+        return dpp_mov<kDppXor1>(x);
+    } else if constexpr (K == 2) {
+        return dpp_mov<kDppXor2>(x);
+    } else if constexpr (K == 4) {
+        int t = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x12C, 0xF, 0x5, false);
+        t = __builtin_amdgcn_update_dpp(t, __float_as_int(x), 0x124, 0xF, 0xA, false);
+        return __int_as_float(t);
+    } else if constexpr (K == 8) {
+        return dpp_mov<0x128>(x);
+    } else {
+        static_assert(K == 16, "lane_xor");
+        return __shfl_xor(x, 16, kWave);
+    }
+}
+
+// Lane K of each aligned group of L lanes (L in {8, 16, 32}, K < 8), for every lane
+// of the group. L = 16 and 32 use row_newbcast (each 16-lane row takes its own lane
+// K; in a 32-lane group both rows hold the same value wherever this is used). L = 8
+// broadcasts each half row separately under bank masks.
+template <int K, int L>
+__device__ __forceinline__ float group_bcast(float x) {
+    static_assert(K < 8, "lane");
+    if constexpr (L == 8) {
+        int t = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + K, 0xF, 0x3, false);
+        t = __builtin_amdgcn_update_dpp(t, __float_as_int(x), 0x158 + K, 0xF, 0xC, false);
+        return __int_as_float(t);
+    } else {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + K, 0xF, 0xF, true));
+    }
+}
+
+// Sum of per-head partial dot products over one row's L lanes (L in {8, 16, 32}),
+// scattered by head. On entry d[r] is this lane's partial for head r ^ (lane & (G-1))
+// (the caller loads q in that lane-dependent order). Head bit b pairs lane with lane
+// XOR 2^b: each lane keeps the registers whose bit b is clear and adds its partner's
+// register with bit b set, which holds the same head, so no select is needed. The
+// remaining lane bits are summed in full: rotations by 2^b inside the 16-lane row
+// (their offsets cover every lane with the same low bits), or XOR partners where
+// the group is 8 lanes wide. On return d[0] is the full dot product for head
+// (lane & (G-1)), the same in every lane of the row that holds that head.
+template <int G, int L>
+__device__ __forceinline__ void row_reduce_scatter(float (&d)[G]) {
+    static_assert(L == 8 || L == 16 || L == 32, "row size");
+    static_assert(G <= L, "heads per row");
+    if constexpr (G >= 2) {
+#pragma unroll
+        for (int r = 0; r < G; r += 2) d[r] += lane_xor<1>(d[r + 1]);
+    }
+    if constexpr (G >= 4) {
+#pragma unroll
+        for (int r = 0; r < G; r += 4) d[r] += lane_xor<2>(d[r + 2]);
+    }
+    if constexpr (G >= 8) {
+        d[0] += lane_xor<4>(d[4]);
+    }
+    if constexpr (L == 8) {
+        if constexpr (G <= 1) d[0] += lane_xor<1>(d[0]);
+        if constexpr (G <= 2) d[0] += lane_xor<2>(d[0]);
+        if constexpr (G <= 4) d[0] += lane_xor<4>(d[0]);
+    } else {
+        if constexpr (G <= 1) d[0] += dpp_mov<0x121>(d[0]);  // row_ror:1
+        if constexpr (G <= 2) d[0] += dpp_mov<0x122>(d[0]);  // row_ror:2
+        if constexpr (G <= 4) d[0] += dpp_mov<0x124>(d[0]);  // row_ror:4
+        d[0] += dpp_mov<0x128>(d[0]);                        // row_ror:8
+        if constexpr (L == 32) d[0] += lane_xor<16>(d[0]);
+    }
 }
 
 // The page's merge operator on states kept in base 2: state (o, l, m) stands for

@@ -25,6 +25,8 @@
 //  - Each wave walks the chunk in blocks of RG x TPL tokens, interleaved with the
 //    other waves. At the end the row groups of a wave, then the waves, are merged
 //    with the same operator (shuffles, then LDS) and the state is written.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -61,8 +63,10 @@ __device__ __forceinline__ float seg_dot(const uint4& qs, const uint4& ks);
 
 template <>
 __device__ __forceinline__ float seg_dot<uint16_t>(const uint4& qs, const uint4& ks) {
-    float acc = 0.0f;
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qs.x), __builtin_bit_cast(bf16x2, ks.x), acc, false);
+    // the first pair in the three-operand form with a zero accumulator (the compiler's
+    // choice, the accumulating two-operand form, needs a separate zeroing move)
+    float acc;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(qs.x), "v"(ks.x));
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qs.y), __builtin_bit_cast(bf16x2, ks.y), acc, false);
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qs.z), __builtin_bit_cast(bf16x2, ks.z), acc, false);
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qs.w), __builtin_bit_cast(bf16x2, ks.w), acc, false);
@@ -121,104 +125,165 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
     const int seg = lane % SEGS;
     const int rg = lane / SEGS;
 
-    // this lane's 16-byte segment of q for each head of the group
+    // the value held by the lanes of this row whose head is h (lane h of the row)
+    auto bcast_head = [](float x, int h) -> float {
+        if constexpr (GT == 1) return x;
+        switch (h) {
+            case 0: return group_bcast<0, SEGS>(x);
+            case 1: return group_bcast<1, SEGS>(x);
+            case 2: return group_bcast<2, SEGS>(x);
+            case 3: return group_bcast<3, SEGS>(x);
+            case 4: return group_bcast<4, SEGS>(x);
+            case 5: return group_bcast<5, SEGS>(x);
+            case 6: return group_bcast<6, SEGS>(x);
+            default: return group_bcast<7, SEGS>(x);
+        }
+    };
+
+    // this lane's 16-byte segment of q for each head of the group, register r holding
+    // head r ^ (lane & (GT - 1)) (the order row_reduce_scatter expects)
     uint4 qs[GT];
     {
         const char* qb = reinterpret_cast<const char*>(p.q) + ((int64_t)b * p.q_sb + (int64_t)h0 * p.q_sh) * (int64_t)sizeof(T);
 #pragma unroll
-        for (int h = 0; h < GT; ++h)
-            qs[h] = *reinterpret_cast<const uint4*>(qb + (int64_t)h * p.q_sh * (int64_t)sizeof(T) + seg * 16);
+        for (int r = 0; r < GT; ++r) {
+            const int h = r ^ (lane & (GT - 1));
+            qs[r] = *reinterpret_cast<const uint4*>(qb + (int64_t)h * p.q_sh * (int64_t)sizeof(T) + seg * 16);
+        }
     }
 
+    // Row addresses: a wave-uniform base (scalar registers) for each row of a block plus
+    // this lane's 32-bit offset inside its row group (row stride x row-group index +
+    // 16-byte segment), so a full block costs no per-lane address arithmetic.
     const int64_t ks_bytes = p.k_st * (int64_t)sizeof(T);
     const int64_t vs_bytes = p.v_st * (int64_t)sizeof(T);
-    const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.k_sb + (int64_t)g * p.k_sh) * (int64_t)sizeof(T) + seg * 16;
-    const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.v_sb + (int64_t)g * p.v_sh) * (int64_t)sizeof(T) + seg * 16;
+    const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.k_sb + (int64_t)g * p.k_sh) * (int64_t)sizeof(T);
+    const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.v_sb + (int64_t)g * p.v_sh) * (int64_t)sizeof(T);
+    const uint32_t koff = (uint32_t)(rg * ks_bytes) + (uint32_t)(seg * 16);
+    const uint32_t voff = (uint32_t)(rg * vs_bytes) + (uint32_t)(seg * 16);
 
-    float m[GT], l[GT], acc[GT][E];
+    // Running state of this lane's row group. The lane keeps the running max and sum
+    // of head (lane & (GT - 1)) (every lane of the row holding that head keeps the same
+    // values) and the weighted V sums of all GT heads for its own channels.
+    float m_own = -INFINITY, l_own = 0.0f, acc[GT][E];
 #pragma unroll
-    for (int h = 0; h < GT; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.0f;
+    for (int h = 0; h < GT; ++h)
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[h][e] = 0.0f;
-    }
 
     const int64_t last = c1 - 1;
-    // rows past the chunk end are clamped to its last row (always valid memory) and masked
-    auto load_block = [&](int64_t t0, uint4 (&kb)[TPL], uint4 (&vb)[TPL]) {
+    // A full block (t0 wave-uniform): uniform row bases plus this lane's offset.
+    auto load_full = [&](int64_t t0, uint4 (&kb)[TPL], uint4 (&vb)[TPL]) {
+#pragma unroll
+        for (int j = 0; j < TPL; ++j) {
+            const char* kr = kbase + (t0 + j * RG) * ks_bytes;
+            const char* vr = vbase + (t0 + j * RG) * vs_bytes;
+            kb[j] = load_stream(reinterpret_cast<const uint4*>(kr + koff));
+            vb[j] = load_stream(reinterpret_cast<const uint4*>(vr + voff));
+        }
+    };
+    // The chunk's last, partial block: rows past its end are clamped to its last row
+    // (always valid memory) and weighted 0.
+    auto load_tail = [&](int64_t t0, uint4 (&kb)[TPL], uint4 (&vb)[TPL]) {
 #pragma unroll
         for (int j = 0; j < TPL; ++j) {
             int64_t t = t0 + j * RG + rg;
             t = t < last ? t : last;
-            kb[j] = load_stream(row_ptr(kbase, t, ks_bytes));
-            vb[j] = load_stream(row_ptr(vbase, t, vs_bytes));
+            kb[j] = load_stream(row_ptr(kbase + seg * 16, t, ks_bytes));
+            vb[j] = load_stream(row_ptr(vbase + seg * 16, t, vs_bytes));
         }
     };
 
-    auto compute_block = [&](int64_t t0, const uint4 (&kb)[TPL], const uint4 (&vb)[TPL]) {
-        float s[TPL][GT];
+    // One block: the logits of the lane's TPL tokens for its own head, the page's
+    // merge of the block into the running state (skipped when no lane's maximum
+    // grew, when every rescale factor is exactly 1), then the weighted V sums of
+    // all GT heads, each token's weight broadcast from a lane that holds its head.
+    const float c = p.scale_log2;
+    auto compute_block = [&](auto masked, int64_t t0, const uint4 (&kb)[TPL], const uint4 (&vb)[TPL]) {
+        float sj[TPL];  // raw q.k of token j for the lane's head
 #pragma unroll
         for (int j = 0; j < TPL; ++j) {
-            const bool valid = t0 + j * RG + rg <= last;
+            float d[GT];
+#pragma unroll
+            for (int r = 0; r < GT; ++r) d[r] = seg_dot<T>(qs[r], kb[j]);
+            row_reduce_scatter<GT, SEGS>(d);
+            sj[j] = d[0];
+        }
+        if constexpr (decltype(masked)::value) {  // tokens past the chunk's end weigh 0
+#pragma unroll
+            for (int j = 0; j < TPL; ++j)
+                if (t0 + j * RG + rg > last) sj[j] = -INFINITY;
+        }
+        float bm = sj[0];
+#pragma unroll
+        for (int j = 1; j < TPL; ++j) bm = fmaxf(bm, sj[j]);
+        const float mn = fmaxf(m_own, bm * c);  // c > 0: the max of the scaled logits
+        if (__builtin_amdgcn_ballot_w64(mn > m_own)) {
+            const float alpha = exp2_fast(m_own - ((mn == -INFINITY) ? 0.0f : mn));
+            l_own *= alpha;
+            m_own = mn;
 #pragma unroll
             for (int h = 0; h < GT; ++h) {
-                const float dot = group_sum<SEGS>(seg_dot<T>(qs[h], kb[j]));
-                s[j][h] = valid ? dot * p.scale_log2 : -INFINITY;
+                const float ah = bcast_head(alpha, h);
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[h][e] *= ah;
             }
         }
+        const float nref = (m_own == -INFINITY) ? 0.0f : -m_own;
 #pragma unroll
-        for (int h = 0; h < GT; ++h) {
-            float bm = s[0][h];
-#pragma unroll
-            for (int j = 1; j < TPL; ++j) bm = fmaxf(bm, s[j][h]);
-            const float mn = fmaxf(m[h], bm);
-            const float ref = (mn == -INFINITY) ? 0.0f : mn;
-            const float alpha = exp2_fast(m[h] - ref);
-            float lsum = 0.0f;
-#pragma unroll
-            for (int j = 0; j < TPL; ++j) {
-                s[j][h] = exp2_fast(s[j][h] - ref);
-                lsum += s[j][h];
-            }
-            l[h] = l[h] * alpha + lsum;
-            m[h] = mn;
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+        for (int j = 0; j < TPL; ++j) {
+            sj[j] = exp2_fast(fmaf(sj[j], c, nref));  // the weight 2^(s c - m)
+            l_own += sj[j];
         }
 #pragma unroll
         for (int j = 0; j < TPL; ++j) {
             float vf[E];
             seg_widen<T>(vb[j], vf);
 #pragma unroll
-            for (int h = 0; h < GT; ++h)
+            for (int h = 0; h < GT; ++h) {
+                const float pw = bcast_head(sj[j], h);
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[h][e] = fmaf(s[j][h], vf[e], acc[h][e]);
+                for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pw, vf[e], acc[h][e]);
+            }
         }
     };
 
-    // Ring of NBUF register buffers: blocks blk+NW, ..., blk+(NBUF-1)NW are in flight
-    // while block blk is computed.
-    const int64_t nblk = (c1 - c0 + BT - 1) / BT;
+    // Full blocks, interleaved over the waves, through a ring of NBUF register
+    // buffers: blocks blk+NW, ..., blk+(NBUF-1)NW are in flight while block blk is
+    // computed. Then the partial last block, if any, by the wave it falls to.
+    const int64_t nfull = (c1 - c0) / BT;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     {
         uint4 kb[NBUF][TPL], vb[NBUF][TPL];
-        int64_t blk = wave;
+        int64_t blk = wave_u;
 #pragma unroll
         for (int s = 0; s < NBUF - 1; ++s)
-            if (blk + s * NW < nblk) load_block(c0 + (blk + s * NW) * BT, kb[s], vb[s]);
-        bool more = blk < nblk;
+            if (blk + s * NW < nfull) load_full(c0 + (blk + s * NW) * BT, kb[s], vb[s]);
+        bool more = blk < nfull;
         while (more) {
 #pragma unroll
             for (int s = 0; s < NBUF; ++s) {
                 if (more) {
                     const int64_t pre = blk + (NBUF - 1) * NW;
-                    if (pre < nblk) load_block(c0 + pre * BT, kb[(s + NBUF - 1) % NBUF], vb[(s + NBUF - 1) % NBUF]);
-                    compute_block(c0 + blk * BT, kb[s], vb[s]);
+                    if (pre < nfull) load_full(c0 + pre * BT, kb[(s + NBUF - 1) % NBUF], vb[(s + NBUF - 1) % NBUF]);
+                    compute_block(std::false_type{}, c0 + blk * BT, kb[s], vb[s]);
                     blk += NW;
-                    more = blk < nblk;
+                    more = blk < nfull;
                 }
             }
         }
+        if (c0 + nfull * BT < c1 && nfull % NW == wave_u) {
+            load_tail(c0 + nfull * BT, kb[0], vb[0]);
+            compute_block(std::true_type{}, c0 + nfull * BT, kb[0], vb[0]);
+        }
+    }
+
+    // every head's running max and sum, in every lane of the row
+    float m[GT], l[GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+        m[h] = bcast_head(m_own, h);
+        l[h] = bcast_head(l_own, h);
     }
 
     // merge the row groups of this wave (lanes that hold the same channels)
