@@ -97,9 +97,9 @@ class CallWorkspace {
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-        keep_pool_cached(dev);
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         if ((e = hipStreamIsCapturing(st_, &cap)) != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+        if (cap == hipStreamCaptureStatusNone) keep_pool_cached(dev);
         if (cap != hipStreamCaptureStatusNone) {
             if ((e = hipMallocAsync(&ptr_, bytes, st_)) != hipSuccess) return hip_fail(e, "hipMallocAsync (workspace)");
             owned_ = true;

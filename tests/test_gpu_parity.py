@@ -221,3 +221,39 @@ def test_shapes_alternate_on_one_stream_and_a_second_stream():
             ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
             dtype = "bf16" if inp.q.dtype == np.uint16 else "f32"
             assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, dtype, what=f"case {i} rep {rep}")
+
+
+@pytest.mark.parametrize("chunk", [512, 16])
+def test_graph_capture_replays_match_eager(chunk):
+    # under capture the library allocates its workspace inside the captured work; chunk 16
+    # gives 313 partial states per row, so the merge also runs in several passes there
+    inp = W.random_decode(B=2, Hq=8, Hkv=2, N=5000, d=128, dtype="bf16", seed=40, seqlens=[5000, 2222])
+    other = W.random_decode(B=2, Hq=8, Hkv=2, N=5000, d=128, dtype="bf16", seed=41, seqlens=[4000, 5000])
+    q, k, v, sl = upload(inp)
+    q2, k2, v2, sl2 = upload(other)
+    ref_o, ref_l = ta.decode(q, k, v, sl, chunk=chunk)
+    ref2_o, ref2_l = ta.decode(q2, k2, v2, sl2, chunk=chunk)
+    out = torch.empty_like(ref_o)
+    lse = torch.empty_like(ref_l)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ta.decode(q, k, v, sl, chunk=chunk, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    log(f"capturing decode, chunk {chunk}")
+    with torch.cuda.graph(g):
+        ta.decode(q, k, v, sl, chunk=chunk, out=out, lse=lse)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {rep}"
+        # eager work on the same stream between replays
+        o2, l2 = ta.decode(q2, k2, v2, sl2, chunk=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, ref2_o) and torch.equal(l2, ref2_l)
+    del g
+    torch.cuda.synchronize()
