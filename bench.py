@@ -83,6 +83,49 @@ def cpu_baseline(inp, wl, budget_s: float):
                       f"{med * 1e3:.1f} ms per step"}
 
 
+def bench_combine(args, dev) -> int:
+    """ta_combine alone on the combine workload: one GPU's share of a 64-shard merge."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import softmax_tree_reduction_amd as ta
+    import workloads as W
+
+    cw = W.COMBINE_WORKLOADS["combine_64x128"]
+    ci = W.make_combine_inputs(cw, args.seed)
+    nbytes = (ci.partial_o.nbytes + ci.partial_lse.nbytes) + cw.B * cw.H * (cw.d + 1) * 4
+    copies = max(1, math.ceil(args.min_rotation_bytes / nbytes))
+    pos = [torch.from_numpy(ci.partial_o).to(dev) for _ in range(copies)]
+    pls = [torch.from_numpy(ci.partial_lse).to(dev) for _ in range(copies)]
+    out = torch.empty(cw.B, cw.H, cw.d, dtype=torch.float32, device=dev)
+    lse = torch.empty(cw.B, cw.H, dtype=torch.float32, device=dev)
+    ta.combine(pos[0], pls[0], out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.combine(ci.partial_o, ci.partial_lse)
+    err = float(np.abs(out.cpu().numpy() - ro).max())
+    lerr = float((np.abs(lse.cpu().numpy() - rl) / np.maximum(1.0, np.abs(rl))).max())
+    if not (err <= 1e-5 and lerr <= 1e-4):
+        print(f"bench: combine parity failed ({err}, {lerr})", file=sys.stderr)
+        return 1
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        ta.combine(pos[i % copies], pls[i % copies], out=out, lse=lse)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        ta.combine(pos[i % copies], pls[i % copies], out=out, lse=lse)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(json.dumps({"mode": "combine", "workload": cw.name, "us_per_call": round(ms * 1e3, 2),
+                      "bytes_per_call": nbytes, "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                      "rows": cw.B * cw.H, "n_parts": cw.n_parts, "copies": copies,
+                      "max_abs_out_err": err, "max_rel_lse_err": lerr}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,9 +137,10 @@ def main() -> int:
     ap.add_argument("--min-rotation-bytes", type=float, default=2 * 2**30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
-    ap.add_argument("--mode", choices=["step", "partial", "copy"], default="step",
+    ap.add_argument("--mode", choices=["step", "partial", "copy", "combine"], default="step",
                     help="step: the benchmark line (default); partial: only the timed partial-kernel launches "
-                         "(for counter runs); copy: a plain device copy of --copy-mib MiB (counter calibration)")
+                         "(for counter runs); copy: a plain device copy of --copy-mib MiB (counter calibration); "
+                         "combine: the standalone ta_combine workload (64 fp32 states per head, 32 x 32 heads)")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
 
@@ -129,6 +173,8 @@ def main() -> int:
         print(json.dumps({"mode": "copy", "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4,
                           "launches": args.warmup + args.steps}))
         return 0
+    if args.mode == "combine":
+        return bench_combine(args, dev)
     print(f"bench: generating {wl.name} (seed {args.seed})", file=sys.stderr, flush=True)
     inp = W.make_decode_inputs(wl, args.seed)
     step_bytes = algorithmic_bytes(wl, inp.seqlens)
@@ -139,7 +185,8 @@ def main() -> int:
         return torch.from_numpy(a).to(dev)
 
     q = to_dev(inp.q)
-    sl = torch.from_numpy(inp.seqlens.astype(np.int32)).to(dev)
+    # ragged batches pass their lengths; when every sequence fills the cache, none are passed
+    sl = torch.from_numpy(inp.seqlens.astype(np.int32)).to(dev) if wl.ragged is not None else None
     k0, v0 = to_dev(inp.k), to_dev(inp.v)
     cache_bytes = k0.numel() * k0.element_size() * 2
     copies = max(1, math.ceil(args.min_rotation_bytes / cache_bytes))

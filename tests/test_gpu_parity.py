@@ -257,3 +257,14 @@ def test_graph_capture_replays_match_eager(chunk):
         assert torch.equal(o2, ref2_o) and torch.equal(l2, ref2_l)
     del g
     torch.cuda.synchronize()
+
+
+def test_out_of_range_seqlens_are_clamped():
+    # lengths outside [0, N] are clamped to it (the header's contract)
+    inp = W.random_decode(B=3, Hq=8, Hkv=2, N=700, d=128, dtype="bf16", seed=50, seqlens=[700, 0, 300])
+    q, k, v, _ = upload(inp)
+    bad = torch.tensor([700 + 1000, -5, 300], dtype=torch.int32, device="cuda")
+    out, lse = ta.decode(q, k, v, bad, chunk=128)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", what="clamped seqlens")
