@@ -56,12 +56,14 @@ def test_ragged_tails_all_dtypes(dtype, d, chunk):
     check_small(inp, chunk, what=f"ragged {dtype} d={d} chunk={chunk}")
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128)])
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (16, 4), (32, 4), (12, 4), (24, 4), (5, 1)])
-def test_gqa_group_sizes(Hq, Hkv):
-    # G = 1, 2, 4, 8 run one workgroup per group; G = 3 and 6 split the group; G = 5 (MQA-like)
-    inp = W.random_decode(B=2, Hq=Hq, Hkv=Hkv, N=1500, d=128, dtype="bf16", seed=Hq * 10 + Hkv,
+def test_gqa_group_sizes(Hq, Hkv, dtype, d):
+    # G = 1, 2, 4, 8 run one workgroup per group; G = 3 and 6 split the group; G = 5 (MQA-like).
+    # bf16 d = 64 has 8-lane rows, f32 d = 128 32-lane rows: each row width meets each head count.
+    inp = W.random_decode(B=2, Hq=Hq, Hkv=Hkv, N=1500, d=d, dtype=dtype, seed=Hq * 10 + Hkv,
                           seqlens=[1500, 999])
-    check_small(inp, 512, what=f"GQA {Hq}/{Hkv}")
+    check_small(inp, 512, what=f"GQA {Hq}/{Hkv} {dtype} d={d}")
 
 
 def test_token_major_strided_cache():
@@ -101,15 +103,16 @@ def test_partial_states_match_oracle_windows():
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
-@pytest.mark.parametrize("n_parts", [1, 3, 5, 7, 64, 128, 200, 1000])
+@pytest.mark.parametrize("n_parts", [1, 3, 5, 7, 64, 128, 200, 1000, 20000])
 @pytest.mark.parametrize("d", [128, 64])
 def test_combine_against_oracle(n_parts, d):
-    wl = W.CombineWorkload("c", B=3, H=5, n_parts=n_parts, d=d)
+    # 20000 leaves take three passes (128 or 256 leaves per workgroup)
+    wl = W.CombineWorkload("c", B=3, H=5 if n_parts < 10000 else 1, n_parts=n_parts, d=d)
     ci = W.make_combine_inputs(wl, n_parts + d)
     pl = ci.partial_lse.copy()
     rng = np.random.default_rng(n_parts)
     pl[rng.random(pl.shape) < 0.2] = -np.inf   # empty states mixed in
-    pl[1, 2] = -np.inf                         # a row with no state at all
+    pl[1, -1] = -np.inf                        # a row with no state at all
     pl[0, 0] = rng.uniform(-80, 80, n_parts).astype(np.float32)  # a wide spread
     log(f"combine n_parts={n_parts} d={d}")
     out, lse = ta.combine(dev_tensor(ci.partial_o), dev_tensor(pl))
