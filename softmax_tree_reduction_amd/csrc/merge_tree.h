@@ -12,7 +12,8 @@
 // Layout: the d channels are split into float4 columns, CG = d / 4 threads per
 // leaf row (one coalesced read per row); the S = NT / CG slots each take R
 // consecutive leaves and run the lowest log2(R) levels in registers, then the
-// slots run the remaining log2(S) levels through LDS. Merging with an empty state
+// slots run the remaining log2(S) levels, by lane shuffles between slots of one
+// wave and through LDS between waves. Merging with an empty state
 // returns the other operand bit for bit, so padding the leaf count up to S * R
 // leaves the tree, and every result, unchanged.
 #pragma once
@@ -106,9 +107,23 @@ __device__ __forceinline__ MState reduce_leaves(const Leaves<R>& lv, MergeSmem<D
         for (int r = 0; r < R; r += 2 * stride) leaf[r] = merge_states(leaf[r], leaf[r + stride]);
     }
     MState st = leaf[0];
-    // remaining levels across slots: slot s merges slot s + t when s is a multiple of 2t
+    // remaining levels across slots: slot s merges slot s + t when s is a multiple of 2t.
+    // Levels whose two slots share a wave exchange states by lane shuffles; the others
+    // go through LDS. (Every lane merges; only the lower slot of each pair goes on.)
+    constexpr int kSlotsPerWave = kWave / CG < S ? kWave / CG : S;
 #pragma unroll
-    for (int t = 1; t < S; t <<= 1) {
+    for (int t = 1; t < kSlotsPerWave; t <<= 1) {
+        MState other;
+        other.o.x = __shfl_xor(st.o.x, t * CG, kWave);
+        other.o.y = __shfl_xor(st.o.y, t * CG, kWave);
+        other.o.z = __shfl_xor(st.o.z, t * CG, kWave);
+        other.o.w = __shfl_xor(st.o.w, t * CG, kWave);
+        other.l = __shfl_xor(st.l, t * CG, kWave);
+        other.m = __shfl_xor(st.m, t * CG, kWave);
+        st = merge_states(st, other);
+    }
+#pragma unroll
+    for (int t = kSlotsPerWave; t < S; t <<= 1) {
         if ((slot & (2 * t - 1)) == t) {
             sm.o[slot][cg] = st.o;
             if (cg == 0) {
