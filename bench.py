@@ -84,7 +84,8 @@ def cpu_baseline(inp, wl, budget_s: float):
 
 
 def bench_combine(args, dev) -> int:
-    """ta_combine alone on the combine workload: one GPU's share of a 64-shard merge."""
+    """ta_combine (or ta_combine_k with --arity K) alone on the combine workload:
+    one GPU's share of a 64-shard merge."""
     import numpy as np
     import torch
 
@@ -100,7 +101,7 @@ def bench_combine(args, dev) -> int:
     pls = [torch.from_numpy(ci.partial_lse).to(dev) for _ in range(copies)]
     out = torch.empty(cw.B, cw.H, cw.d, dtype=torch.float32, device=dev)
     lse = torch.empty(cw.B, cw.H, dtype=torch.float32, device=dev)
-    ta.combine(pos[0], pls[0], out=out, lse=lse)
+    ta.combine(pos[0], pls[0], out=out, lse=lse, arity=args.arity)
     torch.cuda.synchronize()
     ro, rl = oracle.combine(ci.partial_o, ci.partial_lse)
     err = float(np.abs(out.cpu().numpy() - ro).max())
@@ -110,16 +111,17 @@ def bench_combine(args, dev) -> int:
         return 1
     stream = torch.cuda.current_stream(dev)
     for i in range(args.warmup):
-        ta.combine(pos[i % copies], pls[i % copies], out=out, lse=lse)
+        ta.combine(pos[i % copies], pls[i % copies], out=out, lse=lse, arity=args.arity)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for i in range(args.steps):
-        ta.combine(pos[i % copies], pls[i % copies], out=out, lse=lse)
+        ta.combine(pos[i % copies], pls[i % copies], out=out, lse=lse, arity=args.arity)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
-    print(json.dumps({"mode": "combine", "workload": cw.name, "us_per_call": round(ms * 1e3, 2),
+    print(json.dumps({"mode": "combine", "workload": cw.name, "arity": args.arity or 2,
+                      "kernel": "ta_combine_k" if args.arity else "ta_combine", "us_per_call": round(ms * 1e3, 2),
                       "bytes_per_call": nbytes, "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                       "rows": cw.B * cw.H, "n_parts": cw.n_parts, "copies": copies,
                       "max_abs_out_err": err, "max_rel_lse_err": lerr}))
@@ -142,6 +144,8 @@ def main() -> int:
                          "(for counter runs); copy: a plain device copy of --copy-mib MiB (counter calibration); "
                          "combine: the standalone ta_combine workload (64 fp32 states per head, 32 x 32 heads)")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--arity", type=int, default=None,
+                    help="combine mode: time ta_combine_k with this branching factor (2..16) instead of ta_combine")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -125,6 +125,24 @@ int ta_combine(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t
                const ta_tensor* out, const ta_tensor* lse, void* stream);
 
 /*
+ * ta_combine_k - ta_combine with a tree of branching factor `arity` (the page's
+ * k, "Core Innovation 1" step 3: ceil(log_k n_parts) levels).
+ *
+ *   arity        2 <= arity <= 16; other arguments as for ta_combine.
+ *
+ * At each level the nodes are taken in aligned groups of `arity` consecutive
+ * nodes; each group merges left to right into its first node, and a group cut
+ * short by the end of the row merges the nodes it has. Arity 2 is the tree of
+ * ta_combine. One launch merges up to arity^j leaves per row, the largest
+ * power with arity^(j-1) <= 64 (81 to 512 leaves); longer rows run the same tree in
+ * several launches, one per aligned group of that many leaves and then over
+ * the group roots, and take workspace as ta_decode does. Errors: TA_ERR_ARG
+ * for an arity outside [2, 16], otherwise as ta_combine.
+ */
+int ta_combine_k(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts, int32_t arity,
+                 const ta_tensor* out, const ta_tensor* lse, void* stream);
+
+/*
  * ta_partial - the per-chunk partial states alone (the first half of ta_decode).
  *
  * Arguments as for ta_decode, with the outputs

@@ -22,7 +22,7 @@ __all__ = ["decode", "partial", "combine", "TreeAttnError", "library_path", "loa
 TA_OK, TA_ERR_NULL, TA_ERR_SHAPE, TA_ERR_DTYPE, TA_ERR_STRIDE, TA_ERR_ARG, TA_ERR_UNSUPPORTED, TA_ERR_HIP = \
     0, -1, -2, -3, -4, -5, -6, -7
 TA_F32, TA_BF16 = 0, 1
-EXPORTS = ("ta_decode", "ta_combine", "ta_partial", "ta_last_error", "ta_version")
+EXPORTS = ("ta_decode", "ta_combine", "ta_combine_k", "ta_partial", "ta_last_error", "ta_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtreeattn.so")
@@ -69,7 +69,8 @@ def load_library():
             lib.ta_decode.argtypes = [P, P, P, vp, P, P, i32, vp]
             lib.ta_partial.argtypes = [P, P, P, vp, P, P, i32, vp]
             lib.ta_combine.argtypes = [P, P, i32, P, P, vp]
-            for f in (lib.ta_decode, lib.ta_partial, lib.ta_combine):
+            lib.ta_combine_k.argtypes = [P, P, i32, i32, P, P, vp]
+            for f in (lib.ta_decode, lib.ta_partial, lib.ta_combine, lib.ta_combine_k):
                 f.restype = ctypes.c_int
             lib.ta_last_error.restype = ctypes.c_char_p
             lib.ta_version.restype = ctypes.c_int
@@ -182,8 +183,12 @@ def partial(q, k, v, seqlens=None, chunk: int = 2048, partial_o=None, partial_ls
     return partial_o, partial_lse
 
 
-def combine(partial_o, partial_lse, n_parts=None, out=None, lse=None, stream=None):
-    """Tree merge of partial states: returns (out [B, H, d] f32, lse [B, H] f32)."""
+def combine(partial_o, partial_lse, n_parts=None, out=None, lse=None, stream=None, arity=None):
+    """Tree merge of partial states: returns (out [B, H, d] f32, lse [B, H] f32).
+
+    arity None runs ta_combine (the binary tree); an integer in [2, 16] runs
+    ta_combine_k with that branching factor.
+    """
     import torch
     dev = _same_device(partial_o, partial_lse, out, lse)
     B, H, P, d = partial_o.shape
@@ -196,5 +201,8 @@ def combine(partial_o, partial_lse, n_parts=None, out=None, lse=None, stream=Non
     lib = _lib or load_library()
     dpo, dpl, do, dl = _desc(partial_o), _desc(partial_lse), _desc(out), _desc(lse)
     by = ctypes.byref
-    _call(dev, stream, lambda s: lib.ta_combine(by(dpo), by(dpl), int(n_parts), by(do), by(dl), s))
+    if arity is None:
+        _call(dev, stream, lambda s: lib.ta_combine(by(dpo), by(dpl), int(n_parts), by(do), by(dl), s))
+    else:
+        _call(dev, stream, lambda s: lib.ta_combine_k(by(dpo), by(dpl), int(n_parts), int(arity), by(do), by(dl), s))
     return out, lse

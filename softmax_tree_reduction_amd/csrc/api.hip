@@ -138,10 +138,16 @@ class CallWorkspace {
     bool owned_ = false;
 };
 
+// Leaves one merge workgroup takes: the binary kernel's tile (arity 0), or the
+// largest power of `arity` the arity-K kernel holds.
+int64_t merge_span(int64_t d, int arity) {
+    return arity ? ta::combine_k_span((int)d, arity) : ta::combine_max_leaves((int)d);
+}
+
 // Bytes of intermediate states the merge needs when a row has more leaves than one
 // workgroup takes: two buffers of the first pass's output size.
-size_t combine_scratch_bytes(int64_t n_parts, int64_t B, int64_t H, int64_t d) {
-    const int64_t span = ta::combine_max_leaves((int)d);
+size_t combine_scratch_bytes(int64_t n_parts, int64_t B, int64_t H, int64_t d, int arity = 0) {
+    const int64_t span = merge_span(d, arity);
     if (n_parts <= span) return 0;
     const int64_t groups = (n_parts + span - 1) / span;
     return 2 * (size_t)(B * H * groups * (d + 1)) * sizeof(float);
@@ -252,13 +258,24 @@ ta::PartialParams partial_params(const ta_tensor* q, const ta_tensor* k, const t
     return p;
 }
 
+// One pass of the merge: the binary kernel (arity 0) or the arity-K kernel.
+hipError_t launch_pass(const ta::CombineParams& c, int64_t d, int arity, int64_t B, int64_t H, int64_t groups,
+                       int64_t leaves_per_group, hipStream_t stream) {
+    if (!arity) return ta::launch_combine_pass(c, (int)d, (int)B, (int)H, (int)groups, (int)leaves_per_group, stream);
+    int64_t span = arity;  // the smallest power of K (at least K) holding the group's leaves
+    while (span < leaves_per_group) span *= arity;
+    return ta::launch_combine_k_pass(c, (int)d, arity, (int)B, (int)H, (int)groups, (int)span, stream);
+}
+
 // Runs the merge tree over n_parts leaves per row and writes (out, lse).
 // Rows with more leaves than one workgroup takes go through intermediate levels
-// held in `scratch` (combine_scratch_bytes of it).
+// held in `scratch` (combine_scratch_bytes of it). Arity 0 is the binary tree of
+// the merge kernel; 2 <= arity <= 16 runs the arity-K kernel.
 int run_combine(const float* po, const int64_t po_st[3], const float* pl, const int64_t pl_st[3], int64_t n_parts,
                 const int32_t* seqlens, int32_t chunk, int64_t N, int64_t B, int64_t H, int64_t d, float* out,
-                const int64_t out_st[2], float* lse, const int64_t lse_st[2], void* scratch, hipStream_t stream) {
-    const int64_t span = ta::combine_max_leaves((int)d);
+                const int64_t out_st[2], float* lse, const int64_t lse_st[2], void* scratch, hipStream_t stream,
+                int arity = 0) {
+    const int64_t span = merge_span(d, arity);
     const float* cur_o = po;
     const float* cur_l = pl;
     int64_t cur_po[3] = {po_st[0], po_st[1], po_st[2]};
@@ -288,7 +305,7 @@ int run_combine(const float* po, const int64_t po_st[3], const float* pl, const 
         c.lse = nxt_l;
         c.out_sb = H * groups * d; c.out_sh = groups * d; c.out_sg = d;
         c.lse_sb = H * groups; c.lse_sh = groups; c.lse_sg = 1;
-        if ((e = ta::launch_combine_pass(c, (int)d, (int)B, (int)H, (int)groups, (int)span, stream)) != hipSuccess)
+        if ((e = launch_pass(c, d, arity, B, H, groups, span, stream)) != hipSuccess)
             return hip_fail(e, "merge kernel launch");
         cur_o = nxt_o;
         cur_l = nxt_l;
@@ -311,7 +328,7 @@ int run_combine(const float* po, const int64_t po_st[3], const float* pl, const 
     c.lse = lse;
     c.out_sb = out_st[0]; c.out_sh = out_st[1]; c.out_sg = 0;
     c.lse_sb = lse ? lse_st[0] : 0; c.lse_sh = lse ? lse_st[1] : 0; c.lse_sg = 0;
-    if ((e = ta::launch_combine_pass(c, (int)d, (int)B, (int)H, 1, (int)(leaves > 0 ? leaves : 1), stream)) != hipSuccess)
+    if ((e = launch_pass(c, d, arity, B, H, 1, leaves > 0 ? leaves : 1, stream)) != hipSuccess)
         return hip_fail(e, "merge kernel launch");
     return TA_OK;
 }
@@ -370,8 +387,12 @@ int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const 
     return ok();
 }
 
-int ta_combine(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts, const ta_tensor* out,
-               const ta_tensor* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int combine_impl(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts, int arity,
+                 const ta_tensor* out, const ta_tensor* lse, void* stream) {
     int rc;
     if (!partial_o) return fail(TA_ERR_NULL, "partial_o: descriptor is NULL");
     if (partial_o->ndim != 4) return fail(TA_ERR_SHAPE, "partial_o: expected 4 dimensions, got %d", partial_o->ndim);
@@ -385,15 +406,30 @@ int ta_combine(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t
     if (B == 0 || H == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
     CallWorkspace ws(st);
-    if ((rc = ws.acquire(combine_scratch_bytes(n_parts, B, H, d))) != TA_OK) return rc;
+    if ((rc = ws.acquire(combine_scratch_bytes(n_parts, B, H, d, arity))) != TA_OK) return rc;
     const int64_t out_st[2] = {out->stride[0], out->stride[1]};
     const int64_t lse_st[2] = {lse ? lse->stride[0] : 0, lse ? lse->stride[1] : 0};
     rc = run_combine(static_cast<const float*>(partial_o->data), partial_o->stride,
                      static_cast<const float*>(partial_lse->data), partial_lse->stride, n_parts, nullptr, 1, 0, B, H, d,
                      static_cast<float*>(out->data), out_st, lse ? static_cast<float*>(lse->data) : nullptr, lse_st,
-                     ws.get(), st);
+                     ws.get(), st, arity);
     if (rc != TA_OK) return rc;
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ta_combine(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts, const ta_tensor* out,
+               const ta_tensor* lse, void* stream) {
+    return combine_impl(partial_o, partial_lse, n_parts, 0, out, lse, stream);
+}
+
+int ta_combine_k(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts, int32_t arity,
+                 const ta_tensor* out, const ta_tensor* lse, void* stream) {
+    if (arity < 2 || arity > 16) return fail(TA_ERR_ARG, "arity %d outside [2, 16]", arity);
+    return combine_impl(partial_o, partial_lse, n_parts, arity, out, lse, stream);
 }
 
 }  // extern "C"

@@ -53,6 +53,14 @@ int combine_max_leaves(int d);
 hipError_t launch_partial(const PartialParams& p, Dtype dt, int d, int heads_per_wg, int B, int Hq,
                           int n_chunks, hipStream_t stream);
 
+// Leaves per workgroup of the arity-K merge: the largest power of K it takes.
+int combine_k_span(int d, int arity);
+
+// One pass of the arity-K merge tree over `n_parts` leaves per row, in groups of
+// `span` (a power of K) consecutive leaves. Writes one normalised state per group.
+hipError_t launch_combine_k_pass(const CombineParams& p, int d, int arity, int B, int H, int n_groups, int span,
+                                 hipStream_t stream);
+
 // One pass of the merge tree over `n_parts` leaves per row, in groups of up to
 // combine_max_leaves(d) consecutive leaves. Writes one normalised state per group.
 hipError_t launch_combine_pass(const CombineParams& p, int d, int B, int H, int n_groups,

@@ -32,7 +32,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = ta.load_library()
     names = declared_functions()
-    assert {"ta_decode", "ta_combine", "ta_partial", "ta_last_error", "ta_version"} <= names
+    assert {"ta_decode", "ta_combine", "ta_combine_k", "ta_partial", "ta_last_error", "ta_version"} <= names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
     assert set(ta.EXPORTS) == names
@@ -146,6 +146,29 @@ def test_combine_validation():
     assert call_combine(po, pl, 4, out, T([2, 8], ta.TA_BF16))[0] == ta.TA_ERR_DTYPE
     rc, msg = call_combine(T([0, 8, 16, 128], ta.TA_F32), T([0, 8, 16], ta.TA_F32), 4,
                            T([0, 8, 128], ta.TA_F32), T([0, 8], ta.TA_F32))
+    assert rc == ta.TA_OK, msg
+
+
+def call_combine_k(po, pl, n, arity, out, lse):
+    lib = ta.load_library()
+    ref = lambda x: None if x is None else ctypes.byref(x)
+    rc = lib.ta_combine_k(ref(po), ref(pl), n, arity, ref(out), ref(lse), None)
+    return rc, lib.ta_last_error().decode()
+
+
+def test_combine_k_validation():
+    po, pl = T([2, 8, 16, 128], ta.TA_F32), T([2, 8, 16], ta.TA_F32)
+    out, lse = T([2, 8, 128], ta.TA_F32), T([2, 8], ta.TA_F32)
+    for bad in (-1, 0, 1, 17, 1 << 20):
+        rc, msg = call_combine_k(po, pl, 4, bad, out, lse)
+        assert rc == ta.TA_ERR_ARG and "arity" in msg
+    assert call_combine_k(None, pl, 4, 4, out, lse)[0] == ta.TA_ERR_NULL
+    assert call_combine_k(po, pl, 17, 4, out, lse)[0] == ta.TA_ERR_ARG
+    assert call_combine_k(po, T([2, 8, 15], ta.TA_F32), 4, 4, out, lse)[0] == ta.TA_ERR_SHAPE
+    assert call_combine_k(T([2, 8, 16, 96], ta.TA_F32), pl, 4, 8, T([2, 8, 96], ta.TA_F32), lse)[0] == \
+        ta.TA_ERR_UNSUPPORTED
+    rc, msg = call_combine_k(T([2, 0, 16, 128], ta.TA_F32), T([2, 0, 16], ta.TA_F32), 4, 16,
+                             T([2, 0, 128], ta.TA_F32), T([2, 0], ta.TA_F32))
     assert rc == ta.TA_OK, msg
 
 

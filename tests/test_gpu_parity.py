@@ -121,6 +121,75 @@ def test_combine_against_oracle(n_parts, d):
     assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "f32", what=f"combine {n_parts}")
 
 
+def combine_inputs_with_empties(B, H, n_parts, d, seed):
+    ci = W.make_combine_inputs(W.CombineWorkload("c", B=B, H=H, n_parts=n_parts, d=d), seed)
+    pl = ci.partial_lse.copy()
+    rng = np.random.default_rng(seed)
+    pl[rng.random(pl.shape) < 0.2] = -np.inf   # empty states mixed in
+    pl[B - 1, H - 1] = -np.inf                 # a row with no state at all
+    pl[0, 0] = rng.uniform(-80, 80, n_parts).astype(np.float32)  # a wide spread
+    return ci.partial_o, pl
+
+
+def arity_span(d, arity):
+    """Leaves one launch of ta_combine_k takes (either head dimension): the largest
+    power K^j of the arity with K^(j-1) <= 64 first-level nodes."""
+    span = arity
+    while span <= 64:
+        span *= arity
+    return span
+
+
+@pytest.mark.parametrize("arity", [2, 3, 4, 5, 7, 8, 16])
+@pytest.mark.parametrize("n_parts", [1, 7, 16, 17, 64, 65, 300, 5000])
+@pytest.mark.parametrize("d", [128, 64])
+def test_combine_k_against_oracle(arity, n_parts, d):
+    po, pl = combine_inputs_with_empties(3, 4, n_parts, d, 7 * n_parts + arity)
+    log(f"combine_k arity={arity} n_parts={n_parts} d={d}")
+    out, lse = ta.combine(dev_tensor(po), dev_tensor(pl), arity=arity)
+    torch.cuda.synchronize()
+    ro, rl = oracle.combine(po, pl)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "f32", what=f"combine_k {arity} {n_parts}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_combine_k_arity_two_is_the_binary_tree(d):
+    # within one launch both kernels run the same binary tree with the same
+    # operand order, so the results agree bit for bit; at d = 128 both take 128
+    # leaves per launch, so longer rows split into the same passes too
+    more = (1000, 20000) if d == 128 else ()
+    for n_parts in (1, 2, 3, 13, 32, arity_span(d, 2)) + more:
+        po, pl = combine_inputs_with_empties(2, 6, n_parts, d, 100 + n_parts)
+        log(f"combine_k arity=2 vs binary n_parts={n_parts} d={d}")
+        a = ta.combine(dev_tensor(po), dev_tensor(pl), arity=2)
+        b = ta.combine(dev_tensor(po), dev_tensor(pl))
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), n_parts
+
+
+@pytest.mark.parametrize("arity", [2, 3, 4, 16])
+@pytest.mark.parametrize("d", [128, 64])
+def test_combine_k_passes_are_subtrees(arity, d):
+    # A row longer than one launch takes is merged per aligned group of `span`
+    # leaves (a power of the arity, so each group is a whole subtree), and the
+    # group roots are merged by the same tree: the same as doing it by hand.
+    span = arity_span(d, arity)
+    n_parts = span * span + 3 * span + 5     # three passes: span + 4 roots, then 2
+    po, pl = combine_inputs_with_empties(1, 2, n_parts, d, 300 + arity)
+    log(f"combine_k passes arity={arity} d={d} span={span} n_parts={n_parts}")
+    po_d, pl_d = dev_tensor(po), dev_tensor(pl)
+    direct = ta.combine(po_d, pl_d, arity=arity)
+    level = (po_d, pl_d)
+    while level[0].shape[2] > span:
+        n = level[0].shape[2]
+        roots = [ta.combine(level[0][:, :, g:g + span].contiguous(), level[1][:, :, g:g + span].contiguous(),
+                            arity=arity) for g in range(0, n, span)]
+        level = (torch.stack([r[0] for r in roots], 2), torch.stack([r[1] for r in roots], 2))
+    by_hand = ta.combine(level[0], level[1], arity=arity)
+    torch.cuda.synchronize()
+    assert torch.equal(direct[0], by_hand[0]) and torch.equal(direct[1], by_hand[1])
+
+
 def test_combine_uses_leading_parts_only():
     ci = W.make_combine_inputs(W.CombineWorkload("c", B=2, H=3, n_parts=40, d=128), 2)
     po, pl = dev_tensor(ci.partial_o), dev_tensor(ci.partial_lse)
