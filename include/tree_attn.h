@@ -143,6 +143,17 @@ int ta_combine_k(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32
                  const ta_tensor* out, const ta_tensor* lse, void* stream);
 
 /*
+ * ta_combine_chain - the same merge in the order a ring of workers accumulates
+ * it ("The Flaw of Ring Attention During Autoregressive Decoding" in the guide
+ * page: P - 1 sequential hops): out = ((s_0 + s_1) + s_2) + ... + s_{n_parts-1}
+ * under the merge operator, a chain of n_parts - 1 dependent merges where the
+ * tree has ceil(log2 n_parts) levels. A baseline for the tree, not a faster
+ * path. Arguments as for ta_combine; one launch for any n_parts, no workspace.
+ */
+int ta_combine_chain(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts,
+                     const ta_tensor* out, const ta_tensor* lse, void* stream);
+
+/*
  * ta_partial - the per-chunk partial states alone (the first half of ta_decode).
  *
  * Arguments as for ta_decode, with the outputs

@@ -22,7 +22,8 @@ __all__ = ["decode", "partial", "combine", "TreeAttnError", "library_path", "loa
 TA_OK, TA_ERR_NULL, TA_ERR_SHAPE, TA_ERR_DTYPE, TA_ERR_STRIDE, TA_ERR_ARG, TA_ERR_UNSUPPORTED, TA_ERR_HIP = \
     0, -1, -2, -3, -4, -5, -6, -7
 TA_F32, TA_BF16 = 0, 1
-EXPORTS = ("ta_decode", "ta_combine", "ta_combine_k", "ta_partial", "ta_last_error", "ta_version")
+EXPORTS = ("ta_decode", "ta_combine", "ta_combine_k", "ta_combine_chain", "ta_partial", "ta_last_error",
+           "ta_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtreeattn.so")
@@ -70,7 +71,8 @@ def load_library():
             lib.ta_partial.argtypes = [P, P, P, vp, P, P, i32, vp]
             lib.ta_combine.argtypes = [P, P, i32, P, P, vp]
             lib.ta_combine_k.argtypes = [P, P, i32, i32, P, P, vp]
-            for f in (lib.ta_decode, lib.ta_partial, lib.ta_combine, lib.ta_combine_k):
+            lib.ta_combine_chain.argtypes = [P, P, i32, P, P, vp]
+            for f in (lib.ta_decode, lib.ta_partial, lib.ta_combine, lib.ta_combine_k, lib.ta_combine_chain):
                 f.restype = ctypes.c_int
             lib.ta_last_error.restype = ctypes.c_char_p
             lib.ta_version.restype = ctypes.c_int
@@ -187,7 +189,8 @@ def combine(partial_o, partial_lse, n_parts=None, out=None, lse=None, stream=Non
     """Tree merge of partial states: returns (out [B, H, d] f32, lse [B, H] f32).
 
     arity None runs ta_combine (the binary tree); an integer in [2, 16] runs
-    ta_combine_k with that branching factor.
+    ta_combine_k with that branching factor; "chain" runs ta_combine_chain, the
+    sequential order of a ring.
     """
     import torch
     dev = _same_device(partial_o, partial_lse, out, lse)
@@ -203,6 +206,8 @@ def combine(partial_o, partial_lse, n_parts=None, out=None, lse=None, stream=Non
     by = ctypes.byref
     if arity is None:
         _call(dev, stream, lambda s: lib.ta_combine(by(dpo), by(dpl), int(n_parts), by(do), by(dl), s))
+    elif arity == "chain":
+        _call(dev, stream, lambda s: lib.ta_combine_chain(by(dpo), by(dpl), int(n_parts), by(do), by(dl), s))
     else:
         _call(dev, stream, lambda s: lib.ta_combine_k(by(dpo), by(dpl), int(n_parts), int(arity), by(do), by(dl), s))
     return out, lse

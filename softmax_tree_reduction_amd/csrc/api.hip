@@ -391,6 +391,10 @@ int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const 
 
 namespace {
 
+constexpr int kChain = -1;  // combine_impl's arity for the sequential order
+
+// Validates the merge arguments, then runs the merge: the binary tree (arity 0),
+// the arity-K tree (2..16) or the sequential chain (kChain).
 int combine_impl(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts, int arity,
                  const ta_tensor* out, const ta_tensor* lse, void* stream) {
     int rc;
@@ -405,10 +409,26 @@ int combine_impl(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32
     if (B > 65535) return fail(TA_ERR_UNSUPPORTED, "batch %lld exceeds 65535", (long long)B);
     if (B == 0 || H == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
-    CallWorkspace ws(st);
-    if ((rc = ws.acquire(combine_scratch_bytes(n_parts, B, H, d, arity))) != TA_OK) return rc;
     const int64_t out_st[2] = {out->stride[0], out->stride[1]};
     const int64_t lse_st[2] = {lse ? lse->stride[0] : 0, lse ? lse->stride[1] : 0};
+    if (arity == kChain) {
+        ta::CombineParams c{};
+        c.po = static_cast<const float*>(partial_o->data);
+        c.plse = static_cast<const float*>(partial_lse->data);
+        c.po_sb = partial_o->stride[0]; c.po_sh = partial_o->stride[1]; c.po_sp = partial_o->stride[2];
+        c.pl_sb = partial_lse->stride[0]; c.pl_sh = partial_lse->stride[1]; c.pl_sp = partial_lse->stride[2];
+        c.n_parts = n_parts;
+        c.chunk = 1;
+        c.out = static_cast<float*>(out->data);
+        c.lse = lse ? static_cast<float*>(lse->data) : nullptr;
+        c.out_sb = out_st[0]; c.out_sh = out_st[1];
+        c.lse_sb = lse_st[0]; c.lse_sh = lse_st[1];
+        hipError_t e = ta::launch_combine_chain(c, (int)d, (int)B, (int)H, st);
+        if (e != hipSuccess) return hip_fail(e, "chain merge kernel launch");
+        return ok();
+    }
+    CallWorkspace ws(st);
+    if ((rc = ws.acquire(combine_scratch_bytes(n_parts, B, H, d, arity))) != TA_OK) return rc;
     rc = run_combine(static_cast<const float*>(partial_o->data), partial_o->stride,
                      static_cast<const float*>(partial_lse->data), partial_lse->stride, n_parts, nullptr, 1, 0, B, H, d,
                      static_cast<float*>(out->data), out_st, lse ? static_cast<float*>(lse->data) : nullptr, lse_st,
@@ -430,6 +450,11 @@ int ta_combine_k(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32
                  const ta_tensor* out, const ta_tensor* lse, void* stream) {
     if (arity < 2 || arity > 16) return fail(TA_ERR_ARG, "arity %d outside [2, 16]", arity);
     return combine_impl(partial_o, partial_lse, n_parts, arity, out, lse, stream);
+}
+
+int ta_combine_chain(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts,
+                     const ta_tensor* out, const ta_tensor* lse, void* stream) {
+    return combine_impl(partial_o, partial_lse, n_parts, kChain, out, lse, stream);
 }
 
 }  // extern "C"

@@ -219,7 +219,76 @@ int span_kary(int arity) {
     return 0;
 }
 
+// The order in which a ring of P workers accumulates ([guide] "The Flaw of Ring
+// Attention During Autoregressive Decoding": P - 1 sequential hops): the running
+// state takes in one partial state per step, ((s_0 (+) s_1) (+) s_2) (+) ..., a
+// chain of P - 1 dependent merges against the tree's ceil(log2 P) levels. It is
+// the baseline the tree is measured against.
+// One thread per (row, float4 column), kThreads / (D / 4) rows of one sequence per
+// workgroup; the loads of the next batch of leaves are issued before the current
+// batch is merged. Leaves past the end of the row are empty states, which leave
+// the running state bit for bit unchanged.
+template <int D>
+__global__ __launch_bounds__(kThreads) void chain_kernel(CombineParams p, int H) {
+    constexpr int CG = D / 4;
+    constexpr int kRows = kThreads / CG;
+    constexpr int kBatch = 8;
+    const int h = blockIdx.x * kRows + (int)threadIdx.x / CG;
+    const int b = blockIdx.y;
+    const int c = threadIdx.x % CG;
+    if (h >= H) return;  // no barrier below
+    const int valid = p.n_parts;
+    const float* po = p.po + (int64_t)b * p.po_sb + (int64_t)h * p.po_sh + 4 * c;
+    const float* pl = p.plse + (int64_t)b * p.pl_sb + (int64_t)h * p.pl_sh;
+
+    float lse_n[kBatch];
+    float4 o_n[kBatch];
+    auto load = [&](int base) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            lse_n[j] = -INFINITY;
+            o_n[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (base + j < valid) {
+                lse_n[j] = pl[(int64_t)(base + j) * p.pl_sp];
+                o_n[j] = *reinterpret_cast<const float4*>(po + (int64_t)(base + j) * p.po_sp);
+            }
+        }
+    };
+    MState st{make_float4(0.f, 0.f, 0.f, 0.f), 0.0f, -INFINITY};
+    load(0);
+    for (int base = 0; base < valid; base += kBatch) {
+        float lse_c[kBatch];
+        float4 o_c[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            lse_c[j] = lse_n[j];
+            o_c[j] = o_n[j];
+        }
+        load(base + kBatch);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const bool full = lse_c[j] != -INFINITY;
+            const MState leaf{full ? o_c[j] : make_float4(0.f, 0.f, 0.f, 0.f), full ? 1.0f : 0.0f, lse_c[j]};
+            st = (base == 0 && j == 0) ? leaf : merge_states(st, leaf);
+        }
+    }
+    float* out = p.out + (int64_t)b * p.out_sb + (int64_t)h * p.out_sh;
+    float* lse = p.lse ? p.lse + (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh : nullptr;
+    write_root(st, out, lse, c);
+}
+
 }  // namespace
+
+hipError_t launch_combine_chain(const CombineParams& p, int d, int B, int H, hipStream_t stream) {
+    if (d == 128) {
+        hipLaunchKernelGGL(chain_kernel<128>, dim3((H + 7) / 8, B), dim3(kThreads), 0, stream, p, H);
+    } else if (d == 64) {
+        hipLaunchKernelGGL(chain_kernel<64>, dim3((H + 15) / 16, B), dim3(kThreads), 0, stream, p, H);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 int combine_max_leaves(int d) { return (kThreads / (d / 4)) * kMaxR; }
 

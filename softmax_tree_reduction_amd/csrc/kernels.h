@@ -53,6 +53,10 @@ int combine_max_leaves(int d);
 hipError_t launch_partial(const PartialParams& p, Dtype dt, int d, int heads_per_wg, int B, int Hq,
                           int n_chunks, hipStream_t stream);
 
+// The sequential (ring-order) merge of the leading p.n_parts states of every row,
+// one pass, no workspace; p.seqlens is not read.
+hipError_t launch_combine_chain(const CombineParams& p, int d, int B, int H, hipStream_t stream);
+
 // Leaves per workgroup of the arity-K merge: the largest power of K it takes.
 int combine_k_span(int d, int arity);
 

@@ -152,9 +152,10 @@ __device__ __forceinline__ MState tree_merge_row(const float* po, int64_t po_sp,
 }
 
 // Root normalisation (end of "Core Innovation 2"): O = o / l, lse = m + ln l.
-// An empty root gives O = 0 and lse = -inf. Called by the threads of slot 0.
-__device__ __forceinline__ void write_root(const MState& st, float* out_row, float* lse_ptr) {
-    const int cg = threadIdx.x;  // slot 0: tid == column
+// An empty root gives O = 0 and lse = -inf. Called by one thread per float4 column
+// cg of the row (by default the threads of slot 0, whose index is the column).
+__device__ __forceinline__ void write_root(const MState& st, float* out_row, float* lse_ptr,
+                                           int cg = threadIdx.x) {
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     float lse = -INFINITY;
     if (st.l > 0.0f) {

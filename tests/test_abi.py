@@ -32,7 +32,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = ta.load_library()
     names = declared_functions()
-    assert {"ta_decode", "ta_combine", "ta_combine_k", "ta_partial", "ta_last_error", "ta_version"} <= names
+    assert {"ta_decode", "ta_combine", "ta_combine_k", "ta_combine_chain", "ta_partial", "ta_last_error",
+            "ta_version"} <= names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
     assert set(ta.EXPORTS) == names
@@ -169,6 +170,24 @@ def test_combine_k_validation():
         ta.TA_ERR_UNSUPPORTED
     rc, msg = call_combine_k(T([2, 0, 16, 128], ta.TA_F32), T([2, 0, 16], ta.TA_F32), 4, 16,
                              T([2, 0, 128], ta.TA_F32), T([2, 0], ta.TA_F32))
+    assert rc == ta.TA_OK, msg
+
+
+def test_combine_chain_validation():
+    lib = ta.load_library()
+    ref = lambda x: None if x is None else ctypes.byref(x)
+    call = lambda po, pl, n, out, lse: (lib.ta_combine_chain(ref(po), ref(pl), n, ref(out), ref(lse), None),
+                                        lib.ta_last_error().decode())
+    po, pl = T([2, 8, 16, 128], ta.TA_F32), T([2, 8, 16], ta.TA_F32)
+    out, lse = T([2, 8, 128], ta.TA_F32), T([2, 8], ta.TA_F32)
+    assert call(None, pl, 4, out, lse)[0] == ta.TA_ERR_NULL
+    assert call(po, pl, 17, out, lse)[0] == ta.TA_ERR_ARG
+    assert call(po, pl, -1, out, lse)[0] == ta.TA_ERR_ARG
+    assert call(po, T([2, 8, 15], ta.TA_F32), 4, out, lse)[0] == ta.TA_ERR_SHAPE
+    assert call(T([2, 8, 16, 96], ta.TA_F32), pl, 4, T([2, 8, 96], ta.TA_F32), lse)[0] == ta.TA_ERR_UNSUPPORTED
+    assert call(po, pl, 4, out, T([2, 8], ta.TA_BF16))[0] == ta.TA_ERR_DTYPE
+    rc, msg = call(T([0, 8, 16, 128], ta.TA_F32), T([0, 8, 16], ta.TA_F32), 4, T([0, 8, 128], ta.TA_F32),
+                   T([0, 8], ta.TA_F32))
     assert rc == ta.TA_OK, msg
 
 

@@ -190,6 +190,72 @@ def test_combine_k_passes_are_subtrees(arity, d):
     assert torch.equal(direct[0], by_hand[0]) and torch.equal(direct[1], by_hand[1])
 
 
+@pytest.mark.parametrize("n_parts", [0, 1, 2, 7, 9, 64, 1000])
+@pytest.mark.parametrize("d", [128, 64])
+def test_combine_chain_against_oracle(n_parts, d):
+    # 20 heads: 8 (d = 128) or 16 (d = 64) rows per workgroup, the last one ragged
+    po, pl = combine_inputs_with_empties(3, 20, max(n_parts, 1), d, 11 * n_parts + d)
+    log(f"combine_chain n_parts={n_parts} d={d}")
+    out, lse = ta.combine(dev_tensor(po), dev_tensor(pl), n_parts=n_parts, arity="chain")
+    torch.cuda.synchronize()
+    ro, rl = oracle.combine(po[:, :, :n_parts], pl[:, :, :n_parts])
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "f32", what=f"combine_chain {n_parts}")
+
+
+def test_combine_chain_long_row_within_summation_bound():
+    # The chain's last leaf passes through one merge, its first through P - 1, so
+    # its rounding grows like recursive summation: |error| <= (P - 1) u sum|x| for
+    # each of o and l (u = 2^-24), about 2 (P - 1) u max|o_i| on o / l, where the
+    # tree's bound has log2 P in place of P - 1. Checked at that bound with u
+    # doubled for the exponentials; the exact case below is the sharp pin.
+    n_parts, d = 20000, 128
+    po, pl = combine_inputs_with_empties(2, 3, n_parts, d, 4242)
+    out, lse = ta.combine(dev_tensor(po), dev_tensor(pl), arity="chain")
+    torch.cuda.synchronize()
+    ro, rl = oracle.combine(po, pl)
+    out, lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    full = ~np.isneginf(rl)
+    bound = 4 * (n_parts - 1) * 2.0 ** -24 * np.abs(po).max()
+    err = np.abs(out[full] - ro[full]).max()
+    log(f"combine_chain 20000 leaves: max |out - oracle| = {err:.3e}, bound {bound:.3e}")
+    assert err <= bound
+    assert np.isneginf(lse[~full]).all() and (out[~full] == 0).all()
+    assert (np.abs(lse[full] - rl[full]) / np.abs(rl[full])).max() <= 1e-4
+
+
+@pytest.mark.parametrize("arity,n_parts", [("chain", 20000), ("chain", 5), (None, 128), (None, 77), (4, 64), (8, 64),
+                                           (16, 200), (3, 81)])
+def test_merge_is_exact_where_the_arithmetic_is(arity, n_parts):
+    # Equal lse_i make every rescale factor exp2(0) = 1, and o_i on a 2^-6 grid
+    # with |o_i| <= 2 keep every partial sum below 2^16 on that grid: each merge
+    # inside one launch is exact, in any order. The root o / l is then the exact
+    # mean up to the rounding of the final division, for every merge order.
+    d = 128
+    rng = np.random.default_rng(n_parts)
+    po = (rng.integers(-128, 129, size=(2, 3, n_parts, d)) / 64.0).astype(np.float32)
+    pl = np.full((2, 3, n_parts), 3.25, dtype=np.float32)
+    log(f"exact merge arity={arity} n_parts={n_parts}")
+    out, lse = ta.combine(dev_tensor(po), dev_tensor(pl), arity=arity)
+    torch.cuda.synchronize()
+    mean = po.astype(np.float64).mean(axis=2)
+    err = np.abs(out.cpu().numpy() - mean)
+    assert (err <= 4 * 2.0 ** -24 * np.abs(mean) + 1e-12).all(), err.max()
+    assert np.allclose(lse.cpu().numpy(), 3.25 + np.log(n_parts), rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_combine_chain_is_one_group_of_the_k_ary_tree(d):
+    # up to K leaves, the arity-K tree is a single group merged left to right:
+    # the chain, bit for bit
+    for arity, n_parts in ((16, 1), (16, 5), (16, 16), (8, 8), (3, 3), (2, 2)):
+        po, pl = combine_inputs_with_empties(2, 9, n_parts, d, 500 + n_parts)
+        log(f"combine_chain vs arity {arity}, n_parts={n_parts} d={d}")
+        a = ta.combine(dev_tensor(po), dev_tensor(pl), arity="chain")
+        b = ta.combine(dev_tensor(po), dev_tensor(pl), arity=arity)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), (arity, n_parts)
+
+
 def test_combine_uses_leading_parts_only():
     ci = W.make_combine_inputs(W.CombineWorkload("c", B=2, H=3, n_parts=40, d=128), 2)
     po, pl = dev_tensor(ci.partial_o), dev_tensor(ci.partial_lse)
