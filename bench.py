@@ -243,14 +243,19 @@ def main() -> int:
         ta.decode(q, ks[i % copies], vs[i % copies], sl, chunk=chunk, out=out, lse=lse)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # an event after every step as well: the device-side length of each step
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t_wall = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
         ta.decode(q, ks[i % copies], vs[i % copies], sl, chunk=chunk, out=out, lse=lse)
+        marks[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms_step = ev0.elapsed_time(ev1) / args.steps
+    per_step = sorted([ev0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)])
+    pct = lambda f: per_step[min(len(per_step) - 1, int(round(f * (len(per_step) - 1))))] * 1e3
     print(f"bench: {args.steps} steps, {ms_step * 1e3:.1f} us/step (host wall {wall / args.steps * 1e6:.1f} us/step)",
           file=sys.stderr, flush=True)
 
@@ -267,16 +272,43 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_partial = ev0.elapsed_time(ev1) / args.steps
 
-    # ---- merge alone on the partial states
+    # ---- merge alone on the partial states, replayed from a captured graph so that
+    # the host's per-call cost does not hide the device time
     for _ in range(args.warmup):
         ta.combine(po, pl, out=out, lse=lse)
     torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
         ta.combine(po, pl, out=out, lse=lse)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            ta.combine(po, pl, out=out, lse=lse)
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    graph.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_combine = ev0.elapsed_time(ev1) / args.steps
+    del graph
+
+    # ---- practical read ceiling: a plain streaming read of 1 GiB (several times the caches)
+    probe = torch.empty(2**30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        ta.stream_read(probe, sink)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(20):
+        ta.stream_read(probe, sink)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ceiling = probe.numel() / (ev0.elapsed_time(ev1) / 20 * 1e-3) / 1e9
+    del probe
 
     partial_bytes = step_bytes - wl.B * wl.Hq * (wl.d + 1) * 4  # K, V and q; out/lse belong to the merge
     achieved = partial_bytes / (ms_partial * 1e-3) / 1e9
@@ -298,6 +330,9 @@ def main() -> int:
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(ms_step * 1e3, 2),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "us_per_step_dist": {"median": round(pct(0.5), 2), "p10": round(pct(0.1), 2), "p90": round(pct(0.9), 2)},
+        "read_ceiling": {"value": round(ceiling, 1), "unit": "GB/s", "kernel": "ta_stream_read",
+                         "bytes_per_launch": 2**30, "step_pct_of_ceiling": round(100 * gbs / ceiling, 2)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -305,11 +340,15 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d,
                    "context": wl.N, "chunk": chunk, "partials": P, "tree_levels": math.ceil(math.log2(P)) if P > 1 else 0,
-                   "algorithmic_bytes_per_step": step_bytes, "cache_copies": copies, "seed": args.seed},
+                   "algorithmic_bytes_per_step": step_bytes, "cache_copies": copies, "seed": args.seed,
+                   "generator": {"numpy": np.__version__,
+                                 "sha256_first_mib": {n: hashlib.sha256(a.reshape(-1).view(np.uint8)[:2**20].tobytes())
+                                                      .hexdigest()[:16] for n, a in (("q", inp.q), ("k", inp.k), ("v", inp.v))}}},
         "kernels_us": {"partial": round(ms_partial * 1e3, 2), "combine": round(ms_combine * 1e3, 2)},
         "roofline": {"kernel": "partial_kernel", "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": partial_bytes},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": partial_bytes,
+                     "frac_of_read_ceiling": round(achieved / ceiling, 4)},
         "parity": {"rows": len(rows), "max_abs_out_err": perr, "max_rel_lse_err": lerr},
         "cpu_baseline": cpu,
     }

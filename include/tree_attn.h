@@ -168,6 +168,21 @@ int ta_partial(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v,
                const int32_t* seqlens, const ta_tensor* partial_o, const ta_tensor* partial_lse,
                int32_t chunk, void* stream);
 
+/*
+ * ta_stream_read - measurement utility, not part of the decode path: reads
+ * `bytes` bytes of device memory at `buf` once, with the 16-byte nontemporal
+ * loads the partial kernel streams K and V with, and computes nothing from them.
+ * Timing it gives the device's practical read ceiling for this access.
+ *
+ *   buf     device pointer, 16-byte aligned; bytes >= 0, a multiple of 16
+ *   sink    device pointer to one uint32 that the probe may overwrite
+ *   stream  hipStream_t (NULL = default stream); asynchronous
+ *
+ * Returns TA_ERR_NULL or TA_ERR_ARG (size or alignment) without launching,
+ * TA_ERR_HIP on a launch failure, with the message in ta_last_error.
+ */
+int ta_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 /* Message for the last non-zero return on this thread ("" if none). Never NULL. */
 const char* ta_last_error(void);
 

@@ -22,8 +22,8 @@ __all__ = ["decode", "partial", "combine", "TreeAttnError", "library_path", "loa
 TA_OK, TA_ERR_NULL, TA_ERR_SHAPE, TA_ERR_DTYPE, TA_ERR_STRIDE, TA_ERR_ARG, TA_ERR_UNSUPPORTED, TA_ERR_HIP = \
     0, -1, -2, -3, -4, -5, -6, -7
 TA_F32, TA_BF16 = 0, 1
-EXPORTS = ("ta_decode", "ta_combine", "ta_combine_k", "ta_combine_chain", "ta_partial", "ta_last_error",
-           "ta_version")
+EXPORTS = ("ta_decode", "ta_combine", "ta_combine_k", "ta_combine_chain", "ta_partial", "ta_stream_read",
+           "ta_last_error", "ta_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtreeattn.so")
@@ -72,7 +72,9 @@ def load_library():
             lib.ta_combine.argtypes = [P, P, i32, P, P, vp]
             lib.ta_combine_k.argtypes = [P, P, i32, i32, P, P, vp]
             lib.ta_combine_chain.argtypes = [P, P, i32, P, P, vp]
-            for f in (lib.ta_decode, lib.ta_partial, lib.ta_combine, lib.ta_combine_k, lib.ta_combine_chain):
+            lib.ta_stream_read.argtypes = [vp, ctypes.c_int64, vp, vp]
+            for f in (lib.ta_decode, lib.ta_partial, lib.ta_combine, lib.ta_combine_k, lib.ta_combine_chain,
+                      lib.ta_stream_read):
                 f.restype = ctypes.c_int
             lib.ta_last_error.restype = ctypes.c_char_p
             lib.ta_version.restype = ctypes.c_int
@@ -211,3 +213,15 @@ def combine(partial_o, partial_lse, n_parts=None, out=None, lse=None, stream=Non
     else:
         _call(dev, stream, lambda s: lib.ta_combine_k(by(dpo), by(dpl), int(n_parts), int(arity), by(do), by(dl), s))
     return out, lse
+
+
+def stream_read(buf, sink, stream=None):
+    """Read-bandwidth probe (ta_stream_read): streams every byte of the CUDA tensor
+    `buf` once; `sink` is a CUDA tensor of at least 4 bytes the probe may write."""
+    dev = _same_device(buf, sink)
+    if not (buf.is_cuda and sink.is_cuda and buf.is_contiguous() and sink.numel() * sink.element_size() >= 4):
+        raise ValueError("buf must be a contiguous CUDA tensor and sink a CUDA tensor of >= 4 bytes")
+    lib = _lib or load_library()
+    nbytes = buf.numel() * buf.element_size()
+    _call(dev, stream, lambda s: lib.ta_stream_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_int64(nbytes),
+                                                    ctypes.c_void_p(sink.data_ptr()), s))

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libtreeattn.so")
-SOURCES = ["api.hip", "partial.hip", "combine.hip"]
+SOURCES = ["api.hip", "partial.hip", "combine.hip", "probe.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions stay off: all float math is issued as scalar VALU ops.

@@ -452,6 +452,22 @@ int ta_combine_k(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32
     return combine_impl(partial_o, partial_lse, n_parts, arity, out, lse, stream);
 }
 
+int ta_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink) return fail(TA_ERR_NULL, "stream_read: buf or sink is NULL");
+    if (bytes < 0 || bytes % 16 != 0) return fail(TA_ERR_ARG, "stream_read: %lld bytes is not a multiple of 16", (long long)bytes);
+    if (!aligned16(buf)) return fail(TA_ERR_ARG, "stream_read: buf is not 16-byte aligned");
+    if (bytes == 0) return ok();
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "stream_read: device query");
+    const int64_t n16 = bytes / 16;
+    const int64_t grid = 4 * (int64_t)cus < n16 ? 4 * (int64_t)cus : n16;  // four workgroups per CU
+    if ((e = ta::launch_stream_read(buf, n16, sink, (int)grid, static_cast<hipStream_t>(stream))) != hipSuccess)
+        return hip_fail(e, "stream_read kernel launch");
+    return ok();
+}
+
 int ta_combine_chain(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts,
                      const ta_tensor* out, const ta_tensor* lse, void* stream) {
     return combine_impl(partial_o, partial_lse, n_parts, kChain, out, lse, stream);

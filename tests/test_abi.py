@@ -32,8 +32,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = ta.load_library()
     names = declared_functions()
-    assert {"ta_decode", "ta_combine", "ta_combine_k", "ta_combine_chain", "ta_partial", "ta_last_error",
-            "ta_version"} <= names
+    assert {"ta_decode", "ta_combine", "ta_combine_k", "ta_combine_chain", "ta_partial", "ta_stream_read",
+            "ta_last_error", "ta_version"} <= names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
     assert set(ta.EXPORTS) == names
@@ -189,6 +189,21 @@ def test_combine_chain_validation():
     rc, msg = call(T([0, 8, 16, 128], ta.TA_F32), T([0, 8, 16], ta.TA_F32), 4, T([0, 8, 128], ta.TA_F32),
                    T([0, 8], ta.TA_F32))
     assert rc == ta.TA_OK, msg
+
+
+def test_stream_read_validation():
+    lib = ta.load_library()
+    vp = ctypes.c_void_p
+    call = lambda buf, n, sink: (lib.ta_stream_read(vp(buf), ctypes.c_int64(n), vp(sink), None),
+                                 lib.ta_last_error().decode())
+    assert call(None, 16, FAKE)[0] == ta.TA_ERR_NULL
+    assert call(FAKE, 16, None)[0] == ta.TA_ERR_NULL
+    rc, msg = call(FAKE, 24, FAKE)
+    assert rc == ta.TA_ERR_ARG and "multiple of 16" in msg
+    assert call(FAKE, -16, FAKE)[0] == ta.TA_ERR_ARG
+    rc, msg = call(FAKE + 8, 16, FAKE)
+    assert rc == ta.TA_ERR_ARG and "aligned" in msg
+    assert call(FAKE, 0, FAKE) == (ta.TA_OK, "")
 
 
 def test_last_error_is_per_call():

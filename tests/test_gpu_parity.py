@@ -256,6 +256,17 @@ def test_combine_chain_is_one_group_of_the_k_ary_tree(d):
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), (arity, n_parts)
 
 
+def test_stream_read_probe():
+    # zeros XOR to zero, so the probe leaves its sink alone; odd sizes and a
+    # buffer smaller than one workgroup's share run too
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    for n in (16, 4096 + 16, 3 * 2**20 + 48):
+        buf = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        ta.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert sink.item() == 7
+
+
 def test_combine_uses_leading_parts_only():
     ci = W.make_combine_inputs(W.CombineWorkload("c", B=2, H=3, n_parts=40, d=128), 2)
     po, pl = dev_tensor(ci.partial_o), dev_tensor(ci.partial_lse)
