@@ -55,12 +55,19 @@ def _load():
             lib.oracle_combine.argtypes = [p, p, i64, i64, i64, dp, dp]
             lib.oracle_combine.restype = ctypes.c_int
             lib.oracle_num_threads.restype = ctypes.c_int
+            lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_num_threads.restype = None
             _lib = lib
     return _lib
 
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for later calls (timing only: results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _ptr(a: np.ndarray):

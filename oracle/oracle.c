@@ -58,6 +58,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Sets the number of OpenMP threads later calls use (for timing; results do not
+   depend on it). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Exact decode attention for selected (batch, query head) rows.
  *

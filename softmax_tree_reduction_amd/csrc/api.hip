@@ -63,21 +63,6 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(TA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Keep freed workspace in the device's default pool between calls.
-void keep_pool_cached(int device) {
-    static std::mutex mu;
-    static bool done[64] = {};
-    if (device < 0 || device >= 64) return;
-    std::lock_guard<std::mutex> lock(mu);
-    if (done[device]) return;
-    hipMemPool_t pool;
-    if (hipDeviceGetDefaultMemPool(&pool, device) == hipSuccess) {
-        uint64_t threshold = UINT64_MAX;
-        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &threshold);
-    }
-    done[device] = true;
-}
-
 // Device scratch of one call, ordered on the call's stream. Outside graph capture
 // it is a buffer kept per (device, stream) and grown when a call needs more, so a
 // steady decode loop allocates nothing; work on one stream runs in order, so calls
@@ -99,7 +84,6 @@ class CallWorkspace {
         if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         if ((e = hipStreamIsCapturing(st_, &cap)) != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
-        if (cap == hipStreamCaptureStatusNone) keep_pool_cached(dev);
         if (cap != hipStreamCaptureStatusNone) {
             if ((e = hipMallocAsync(&ptr_, bytes, st_)) != hipSuccess) return hip_fail(e, "hipMallocAsync (workspace)");
             owned_ = true;
