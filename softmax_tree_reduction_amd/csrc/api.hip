@@ -128,6 +128,17 @@ int64_t merge_span(int64_t d, int arity) {
     return arity ? ta::combine_k_span((int)d, arity) : ta::combine_max_leaves((int)d);
 }
 
+// The merge's first pass puts one workgroup per group of leaves on the grid's third
+// dimension, which holds at most 65535.
+int check_merge_groups(int64_t n_parts, int64_t d, int arity) {
+    const int64_t span = merge_span(d, arity);
+    const int64_t groups = (n_parts + span - 1) / span;
+    if (groups > 65535)
+        return fail(TA_ERR_UNSUPPORTED, "%lld states per row exceed the merge's %lld (%lld groups of %lld)",
+                    (long long)n_parts, (long long)(65535 * span), (long long)groups, (long long)span);
+    return TA_OK;
+}
+
 // Bytes of intermediate states the merge needs when a row has more leaves than one
 // workgroup takes: two buffers of the first pass's output size.
 size_t combine_scratch_bytes(int64_t n_parts, int64_t B, int64_t H, int64_t d, int arity = 0) {
@@ -351,6 +362,7 @@ int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t P = s.N > 0 ? (s.N + chunk - 1) / chunk : 1;  // N = 0: one empty state per row
     const size_t part_bytes = (size_t)(s.B * s.Hq * P * (s.d + 1)) * sizeof(float);
+    if ((rc = check_merge_groups(P, s.d, 0)) != TA_OK) return rc;
     const size_t merge_bytes = combine_scratch_bytes(P, s.B, s.Hq, s.d);
     CallWorkspace ws(st);
     if ((rc = ws.acquire(part_bytes + merge_bytes)) != TA_OK) return rc;
@@ -411,6 +423,7 @@ int combine_impl(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32
         if (e != hipSuccess) return hip_fail(e, "chain merge kernel launch");
         return ok();
     }
+    if ((rc = check_merge_groups(n_parts, d, arity)) != TA_OK) return rc;
     CallWorkspace ws(st);
     if ((rc = ws.acquire(combine_scratch_bytes(n_parts, B, H, d, arity))) != TA_OK) return rc;
     rc = run_combine(static_cast<const float*>(partial_o->data), partial_o->stride,

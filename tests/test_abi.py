@@ -206,6 +206,24 @@ def test_stream_read_validation():
     assert call(FAKE, 0, FAKE) == (ta.TA_OK, "")
 
 
+def test_merge_group_limit_is_refused_before_launch():
+    # more leaves per row than 65535 workgroups of the first merge pass can take
+    n = 65535 * 128 + 1
+    po, pl = T([1, 1, n, 128], ta.TA_F32), T([1, 1, n], ta.TA_F32)
+    out, lse = T([1, 1, 128], ta.TA_F32), T([1, 1], ta.TA_F32)
+    rc, msg = call_combine(po, pl, n, out, lse)
+    assert rc == ta.TA_ERR_UNSUPPORTED and "exceed" in msg
+    assert call_combine(po, pl, n - 1, out, lse)[0] != ta.TA_ERR_UNSUPPORTED
+    nk = 65535 * 512 + 1  # arity 8 takes 8^3 = 512 leaves per group
+    pok, plk = T([1, 1, nk, 128], ta.TA_F32), T([1, 1, nk], ta.TA_F32)
+    rc, msg = call_combine_k(pok, plk, nk, 8, out, lse)
+    assert rc == ta.TA_ERR_UNSUPPORTED and "exceed" in msg
+    assert call_combine_k(po, pl, n, 8, out, lse)[0] != ta.TA_ERR_UNSUPPORTED
+    a = good(B=1, Hq=8, Hkv=8, N=n, d=128)  # chunk 1: one state per token
+    rc, msg = call_decode(a, chunk=1)
+    assert rc == ta.TA_ERR_UNSUPPORTED and "exceed" in msg
+
+
 def test_last_error_is_per_call():
     rc, msg = call_decode(good(), chunk=0)
     assert rc != 0 and msg
