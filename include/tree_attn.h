@@ -91,7 +91,9 @@ enum {
  *   lse      [B, Hq]         f32, natural-log log-sum-exp of the logits, or NULL
  *   chunk    tokens per partial state, >= 1
  *
- * Supported: d in {64, 128}; Hq a multiple of Hkv; B <= 65535; Hq <= 65535.
+ * Supported: d in {64, 128}; Hq a multiple of Hkv; B <= 65535; Hq <= 65535;
+ * P = ceil(N / chunk) <= 65535 * 128 (d = 128) or 65535 * 256 (d = 64), the
+ * states one merge pass takes (TA_ERR_UNSUPPORTED beyond).
  * Needs Hq * P * (d + 1) * 4 bytes of device workspace per sequence
  * (P = ceil(N / chunk)). The library keeps one workspace buffer per (device,
  * stream), allocated with hipMallocAsync on that stream the first time it is
@@ -118,8 +120,9 @@ int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v,
  * Leaf i covers the i-th state; level t of the tree merges node i with node
  * i + 2^t for every i that is a multiple of 2^(t+1) (a node without a partner
  * passes up unchanged), giving ceil(log2 n_parts) levels.
- * Supported: d in {64, 128}. n_parts above 128 (d = 128) or 256 (d = 64) runs
- * the same tree in several launches and takes workspace as ta_decode does.
+ * Supported: d in {64, 128}; n_parts <= 65535 * 128 (d = 128) or 65535 * 256
+ * (d = 64). n_parts above 128 (d = 128) or 256 (d = 64) runs the same tree in
+ * several launches and takes workspace as ta_decode does.
  */
 int ta_combine(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts,
                const ta_tensor* out, const ta_tensor* lse, void* stream);
@@ -136,8 +139,9 @@ int ta_combine(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t
  * ta_combine. One launch merges up to arity^j leaves per row, the largest
  * power with arity^(j-1) <= 64 (81 to 512 leaves); longer rows run the same tree in
  * several launches, one per aligned group of that many leaves and then over
- * the group roots, and take workspace as ta_decode does. Errors: TA_ERR_ARG
- * for an arity outside [2, 16], otherwise as ta_combine.
+ * the group roots, and take workspace as ta_decode does; at most 65535 such
+ * groups per row. Errors: TA_ERR_ARG for an arity outside [2, 16], otherwise
+ * as ta_combine.
  */
 int ta_combine_k(const ta_tensor* partial_o, const ta_tensor* partial_lse, int32_t n_parts, int32_t arity,
                  const ta_tensor* out, const ta_tensor* lse, void* stream);
