@@ -349,7 +349,16 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
 
 template <typename T, int D, int GT, int NW, int TPL, int NBUF>
 __global__ __launch_bounds__(NW * kWave) void partial_kernel(PartialParams p) {
-    const int chunk_idx = blockIdx.x;
+    // Workgroups are handed to the eight XCDs in turn, so with the chunk index fastest
+    // (and a multiple of 8 chunks per row) XCD k takes chunks k, k + 8, ... of every
+    // row. In a ragged batch each row's last, partly used group of 8 chunks would
+    // then always load the low-numbered XCDs; rotating the order by one XCD per row
+    // spreads that remainder evenly. Any permutation of a row's chunks is correct.
+    int chunk_idx = blockIdx.x;
+    if (p.seqlens && (gridDim.x & 7u) == 0) {
+        const unsigned row = blockIdx.y + gridDim.y * blockIdx.z;
+        chunk_idx = (int)((blockIdx.x & ~7u) | ((blockIdx.x - row) & 7u));
+    }
     const int h0 = blockIdx.y * GT;
     const int b = blockIdx.z;
     const int g = h0 / p.group;

@@ -48,7 +48,7 @@ def test_tiny_f32_workload_full():
 
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
-@pytest.mark.parametrize("chunk", [1, 37, 256, 2048, 100000])
+@pytest.mark.parametrize("chunk", [1, 37, 256, 375, 2048, 100000])
 def test_ragged_tails_all_dtypes(dtype, d, chunk):
     # 3000 tokens: several tiles, a ragged tail, one empty sequence, one shorter than a block
     N = 3000
@@ -85,14 +85,16 @@ def test_single_chunk_pins_partial_kernel():
 
 
 def test_partial_states_match_oracle_windows():
-    inp = W.random_decode(B=2, Hq=8, Hkv=2, N=2000, d=128, dtype="bf16", seed=10, seqlens=[2000, 700])
+    # 8 chunks per row of a ragged batch: the chunk order is rotated per row across
+    # the XCDs, and every state must still land in its own slot
+    inp = W.random_decode(B=3, Hq=8, Hkv=2, N=2400, d=128, dtype="bf16", seed=10, seqlens=[2400, 700, 2399])
     chunk = 300
     q, k, v, sl = upload(inp)
     po, pl = ta.partial(q, k, v, sl, chunk=chunk)
     torch.cuda.synchronize()
     po, pl = po.cpu().numpy(), pl.cpu().numpy()
-    P = -(-2000 // chunk)
-    assert po.shape == (2, 8, P, 128)
+    P = -(-2400 // chunk)
+    assert po.shape == (3, 8, P, 128) and P == 8
     for i in range(P):
         ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens, t_begin=i * chunk, t_end=(i + 1) * chunk)
         assert_close(po[:, :, i], pl[:, :, i], ro, rl, "bf16", what=f"partial {i}")
