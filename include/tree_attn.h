@@ -23,8 +23,9 @@
  *    points to device memory on the current HIP device. The descriptors are
  *    read during the call only; the library keeps no pointer after it returns.
  *    The caller owns every tensor.
- *  - Strides are in elements. The last dimension (the head dimension d) must
- *    be contiguous (stride 1), and every row start must be 16-byte aligned.
+ *  - Strides are in elements, never negative. In q, k, v, out and partial_o the
+ *    last dimension (the head dimension d) must be contiguous (stride 1) and
+ *    every row start 16-byte aligned; lse and partial_lse take any strides.
  *  - Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
  *  - The log-sum-exp is a natural logarithm. A sequence with no tokens (and a
  *    partial state of an empty chunk) has out = 0 and lse = -inf.

@@ -35,8 +35,10 @@ int64_t elem_size(int32_t dtype) { return dtype == TA_BF16 ? 2 : 4; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Checks ndim, dtype, a contiguous last dimension, and 16-byte aligned rows.
-int check_tensor(const ta_tensor* t, const char* name, int ndim, bool need_rows_aligned) {
+// Checks ndim, dtype and non-negative sizes and strides. Tensors whose last
+// dimension is the head dimension (rows_of_d) also need it contiguous and every
+// row 16-byte aligned; the lse tensors take any strides.
+int check_tensor(const ta_tensor* t, const char* name, int ndim, bool rows_of_d) {
     if (!t) return fail(TA_ERR_NULL, "%s: descriptor is NULL", name);
     if (!t->data) return fail(TA_ERR_NULL, "%s: data pointer is NULL", name);
     if (t->ndim != ndim) return fail(TA_ERR_SHAPE, "%s: expected %d dimensions, got %d", name, ndim, t->ndim);
@@ -45,17 +47,16 @@ int check_tensor(const ta_tensor* t, const char* name, int ndim, bool need_rows_
         if (t->shape[i] < 0) return fail(TA_ERR_SHAPE, "%s: negative size in dimension %d", name, i);
         if (t->stride[i] < 0) return fail(TA_ERR_STRIDE, "%s: negative stride in dimension %d", name, i);
     }
+    if (!rows_of_d) return TA_OK;
     if (t->shape[ndim - 1] > 1 && t->stride[ndim - 1] != 1)
         return fail(TA_ERR_STRIDE, "%s: the last dimension must be contiguous (stride 1), got %lld", name,
                     (long long)t->stride[ndim - 1]);
-    if (need_rows_aligned) {
-        if (!aligned16(t->data)) return fail(TA_ERR_STRIDE, "%s: data pointer is not 16-byte aligned", name);
-        const int64_t es = elem_size(t->dtype);
-        for (int i = 0; i < ndim - 1; ++i)
-            if (t->shape[i] > 1 && (t->stride[i] * es) % 16 != 0)
-                return fail(TA_ERR_STRIDE, "%s: stride of dimension %d (%lld elements) is not a multiple of 16 bytes",
-                            name, i, (long long)t->stride[i]);
-    }
+    if (!aligned16(t->data)) return fail(TA_ERR_STRIDE, "%s: data pointer is not 16-byte aligned", name);
+    const int64_t es = elem_size(t->dtype);
+    for (int i = 0; i < ndim - 1; ++i)
+        if (t->shape[i] > 1 && (t->stride[i] * es) % 16 != 0)
+            return fail(TA_ERR_STRIDE, "%s: stride of dimension %d (%lld elements) is not a multiple of 16 bytes",
+                        name, i, (long long)t->stride[i]);
     return TA_OK;
 }
 

@@ -224,6 +224,19 @@ def test_merge_group_limit_is_refused_before_launch():
     assert rc == ta.TA_ERR_UNSUPPORTED and "exceed" in msg
 
 
+def test_lse_tensors_take_any_strides():
+    # lse and partial_lse have no head dimension: non-unit and unaligned strides pass
+    # validation (the calls then fail only for lack of a GPU, or succeed on one)
+    po = T([2, 8, 16, 128], ta.TA_F32)
+    pl = T([2, 8, 16], ta.TA_F32, stride=[1, 2, 16], data=FAKE + 4)
+    out = T([2, 8, 128], ta.TA_F32)
+    lse = T([2, 8], ta.TA_F32, stride=[3, 30], data=FAKE + 4)
+    rc, msg = call_combine(po, pl, 16, out, lse)
+    assert rc not in (ta.TA_ERR_STRIDE, ta.TA_ERR_SHAPE, ta.TA_ERR_DTYPE, ta.TA_ERR_ARG), msg
+    bad = T([2, 8], ta.TA_F32, stride=[8, -1])
+    assert call_combine(po, pl, 16, out, bad)[0] == ta.TA_ERR_STRIDE
+
+
 def test_last_error_is_per_call():
     rc, msg = call_decode(good(), chunk=0)
     assert rc != 0 and msg

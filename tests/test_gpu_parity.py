@@ -419,3 +419,79 @@ def test_out_of_range_seqlens_are_clamped():
     torch.cuda.synchronize()
     ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
     assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", what="clamped seqlens")
+
+
+# ---------------------------------------------------------------- strides, determinism, capture
+
+def test_combine_reads_strided_partials():
+    # states stored leaf-major [P, B, H, d] and passed as a permuted [B, H, P, d] view
+    P, B, H, d = 200, 2, 3, 128
+    po_np, pl_np = combine_inputs_with_empties(B, H, P, d, 61)
+    po_lm = dev_tensor(np.ascontiguousarray(po_np.transpose(2, 0, 1, 3)))   # [P, B, H, d]
+    pl_lm = dev_tensor(np.ascontiguousarray(pl_np.transpose(2, 0, 1)))      # [P, B, H]
+    po_v, pl_v = po_lm.permute(1, 2, 0, 3), pl_lm.permute(1, 2, 0)
+    assert not po_v.is_contiguous()
+    for arity in (None, 4, "chain"):
+        out, lse = ta.combine(po_v, pl_v, arity=arity)
+        torch.cuda.synchronize()
+        ro, rl = oracle.combine(po_np, pl_np)
+        assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "f32", what=f"strided combine {arity}")
+
+
+def test_decode_with_strided_q_and_output_slices():
+    inp = W.random_decode(B=2, Hq=8, Hkv=2, N=1200, d=128, dtype="bf16", seed=62, seqlens=[1200, 555])
+    q, k, v, sl = upload(inp)
+    # q inside a wider buffer ([B, Hq, 2d], every other d-block), out and lse inside bigger tensors
+    wide = torch.zeros(2, 8, 256, dtype=torch.bfloat16, device="cuda")
+    wide[:, :, 128:] = q
+    q_view = wide[:, :, 128:]
+    big_out = torch.full((2, 10, 128), 5.0, device="cuda")
+    big_lse = torch.full((2, 10, 3), 5.0, device="cuda")
+    out_view, lse_view = big_out[:, 1:9], big_lse[:, 1:9, 1]  # lse with a token stride of 3
+    ta.decode(q_view, k, v, sl, chunk=256, out=out_view, lse=lse_view)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+    assert_close(out_view.cpu().numpy(), lse_view.cpu().numpy(), ro, rl, "bf16", what="strided q / output views")
+    # nothing outside the views was written
+    assert torch.all(big_out[:, 0] == 5.0) and torch.all(big_out[:, 9] == 5.0)
+    assert torch.all(big_lse[:, :, 0] == 5.0) and torch.all(big_lse[:, :, 2] == 5.0)
+    assert torch.all(big_lse[:, 0, 1] == 5.0) and torch.all(big_lse[:, 9, 1] == 5.0)
+
+
+@pytest.mark.parametrize("arity", [3, 8, "chain"])
+def test_merge_variants_bitwise_deterministic(arity):
+    po_np, pl_np = combine_inputs_with_empties(4, 8, 700, 128, 63)
+    po, pl = dev_tensor(po_np), dev_tensor(pl_np)
+    a = ta.combine(po, pl, arity=arity)
+    b = ta.combine(po, pl, arity=arity)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_graph_capture_of_multipass_arity_merge():
+    # 5000 leaves at arity 4 (256 per launch) take two passes through workspace
+    # allocated inside the capture; replays must match the eager result every time
+    po_np, pl_np = combine_inputs_with_empties(2, 3, 5000, 64, 64)
+    po, pl = dev_tensor(po_np), dev_tensor(pl_np)
+    ref_o, ref_l = ta.combine(po, pl, arity=4)
+    out, lse = torch.empty_like(ref_o), torch.empty_like(ref_l)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ta.combine(po, pl, out=out, lse=lse, arity=4)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    log("capturing a two-pass arity-4 merge")
+    with torch.cuda.graph(g):
+        ta.combine(po, pl, out=out, lse=lse, arity=4)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {rep}"
+        o2, _ = ta.combine(po[:, :, :77].contiguous(), pl[:, :, :77].contiguous(), arity=4)  # eager work between
+        torch.cuda.synchronize()
+    del g
+    torch.cuda.synchronize()
