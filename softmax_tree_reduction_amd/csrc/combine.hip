@@ -1,22 +1,27 @@
-// Tree merge of partial states for gfx950.
+// Merges of partial states for gfx950.
 //
 // Section "Core Innovation 1" step 3 of "Tree Attention Guide: Topology-Aware LLM
 // Decoding" reduces the partial states up a tree of depth ceil(log_k P); section
 // "Core Innovation 2" gives the merge applied at each node:
 //   m = max(m_A, m_B), alpha = exp(m_A - m), beta = exp(m_B - m),
 //   l = alpha l_A + beta l_B, o = alpha o_A + beta o_B,
-// and the normalisation O = o / l at the root. Here k = 2 and the tree is fixed:
-// at level t, node i merges node i + 2^t whenever i is a multiple of 2^(t+1).
+// and the normalisation O = o / l at the root.
 //
 // A stored partial is normalised, (o_i, lse_i); it enters the tree as the page's
 // tuple (o_i, 1, lse_i), which is the same state. A leaf with lse_i = -inf is
 // the empty state (0, 0, -inf).
 //
-// One workgroup of 256 threads merges up to S * R leaves of one (sequence, head)
-// row with the binary tree of merge_tree.h; combine_k_kernel runs the same page's
-// tree at a branching factor K >= 2 through LDS. Rows with more leaves than one workgroup
-// takes are merged in several passes over aligned groups of leaves, which is the
-// same tree.
+// Three kernels:
+//  - combine_kernel: the binary tree (k = 2), fixed: at level t, node i merges
+//    node i + 2^t whenever i is a multiple of 2^(t+1). One workgroup of 256
+//    threads merges up to S * R leaves of one (sequence, head) row with the tree
+//    of merge_tree.h. This is the merge of the decode path.
+//  - combine_k_kernel: the same page's tree at a branching factor 2 <= K <= 16.
+//  - chain_kernel: the states folded one after another, the order of a ring: the
+//    baseline the tree is measured against.
+// Rows with more leaves than one workgroup of a tree kernel takes are merged in
+// several passes over aligned groups of leaves, each group a whole subtree, which
+// is the same tree.
 #include "kernels.h"
 #include "merge_tree.h"
 
