@@ -93,8 +93,9 @@ enum {
  *   chunk    tokens per partial state, >= 1
  *
  * Supported: d in {64, 128}; Hq a multiple of Hkv; B <= 65535; Hq <= 65535;
- * P = ceil(N / chunk) <= 65535 * 128 (d = 128) or 65535 * 256 (d = 64), the
- * states one merge pass takes (TA_ERR_UNSUPPORTED beyond).
+ * a token stride of k and v below 256 MiB; P = ceil(N / chunk) <= 65535 * 128
+ * (d = 128) or 65535 * 256 (d = 64), the states one merge pass takes
+ * (TA_ERR_UNSUPPORTED beyond any of these).
  * Needs Hq * P * (d + 1) * 4 bytes of device workspace per sequence
  * (P = ceil(N / chunk)). The library keeps one workspace buffer per (device,
  * stream), allocated with hipMallocAsync on that stream the first time it is
