@@ -495,3 +495,26 @@ def test_graph_capture_of_multipass_arity_merge():
         torch.cuda.synchronize()
     del g
     torch.cuda.synchronize()
+
+
+def test_binding_raises_the_library_code_and_message():
+    inp = W.random_decode(B=1, Hq=8, Hkv=2, N=256, d=128, dtype="bf16", seed=70)
+    q, k, v, _ = upload(inp)
+    with pytest.raises(ValueError):  # host tensors never reach the library
+        ta.decode(q.cpu(), k, v, None, chunk=64)
+    with pytest.raises(ta.TreeAttnError) as e:
+        ta.decode(q, k, v, None, chunk=0)
+    assert e.value.code == ta.TA_ERR_ARG and "chunk" in str(e.value)
+    with pytest.raises(ta.TreeAttnError) as e:
+        ta.decode(q, k[:, :, :, :64], v, None, chunk=64)  # k and v shapes differ
+    assert e.value.code == ta.TA_ERR_SHAPE
+    po = torch.zeros(1, 8, 4, 128, device="cuda")
+    pl = torch.zeros(1, 8, 4, device="cuda")
+    with pytest.raises(ta.TreeAttnError) as e:
+        ta.combine(po, pl, arity=17)
+    assert e.value.code == ta.TA_ERR_ARG and "arity" in str(e.value)
+    # a failed call leaves the stream usable
+    out, lse = ta.decode(q, k, v, None, chunk=64)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", what="after errors")
