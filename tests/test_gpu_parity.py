@@ -518,3 +518,28 @@ def test_binding_raises_the_library_code_and_message():
     torch.cuda.synchronize()
     ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
     assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", what="after errors")
+
+
+def test_sharded_decode_then_combine_is_the_full_decode():
+    # The multi-GPU split on one device, with public calls only: each "shard" decodes
+    # its own token range of the cache (a strided view, its own lengths), and one
+    # ta_combine over the shard outputs, as leaves (o_r, lse_r), gives the full decode.
+    G, N = 4, 4096
+    inp = W.random_decode(B=3, Hq=32, Hkv=8, N=N, d=128, dtype="bf16", seed=71, seqlens=[4096, 2500, 700])
+    q, k, v, sl = upload(inp)
+    n = N // G
+    outs, lses = [], []
+    for r in range(G):
+        lens = torch.clamp(sl - r * n, 0, n).to(torch.int32)  # shard 3 of sequence 3 is empty
+        o, l = ta.decode(q, k[:, :, r * n:(r + 1) * n], v[:, :, r * n:(r + 1) * n], lens, chunk=256)
+        outs.append(o)
+        lses.append(l)
+    po = torch.stack(outs, dim=2)   # [B, Hq, G, d]
+    pl = torch.stack(lses, dim=2)   # [B, Hq, G]
+    out, lse = ta.combine(po, pl)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", what="shards + combine")
+    full_o, full_l = ta.decode(q, k, v, sl, chunk=256)
+    torch.cuda.synchronize()
+    assert (out - full_o).abs().max().item() < 1e-5 and (lse - full_l).abs().max().item() < 1e-4
