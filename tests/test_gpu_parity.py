@@ -543,3 +543,23 @@ def test_sharded_decode_then_combine_is_the_full_decode():
     full_o, full_l = ta.decode(q, k, v, sl, chunk=256)
     torch.cuda.synchronize()
     assert (out - full_o).abs().max().item() < 1e-5 and (lse - full_l).abs().max().item() < 1e-4
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,chunk", [
+    (65535, 1, 1, 24, 8),      # the largest batch: the partial grid's z and the merge grid's y at 65535
+    (1, 65535, 65535, 8, 4),   # the most query heads: 65535 head groups of one head each
+    (2, 2, 1, 4096 * 8 + 3, 4096),  # 9 chunks of 4096 and a 3-token tail
+])
+def test_grid_limits(B, Hq, Hkv, N, chunk):
+    inp = W.random_decode(B=B, Hq=Hq, Hkv=Hkv, N=N, d=64, dtype="bf16", seed=80,
+                          seqlens=[N - (b % 5) for b in range(B)])
+    log(f"grid limits: B={B} Hq={Hq} Hkv={Hkv} N={N} chunk={chunk}")
+    q, k, v, sl = upload(inp)
+    out, lse = ta.decode(q, k, v, sl, chunk=chunk)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(B * Hq - 64, B * Hq),
+                                     np.random.default_rng(1).choice(B * Hq, 64)]))
+    rows = rows[(rows >= 0) & (rows < B * Hq)]
+    ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens, rows=rows)
+    assert_close(out.reshape(-1, 64)[rows], lse.reshape(-1)[rows], ro, rl, "bf16", what=f"grid limits B={B} Hq={Hq}")
