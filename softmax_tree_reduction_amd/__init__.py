@@ -7,7 +7,8 @@ fallback path.
 
     out, lse = decode(q, k, v, seqlens=None, chunk=2048)
     po, pl   = partial(q, k, v, seqlens=None, chunk=2048)
-    out, lse = combine(po, pl, n_parts=None)
+    out, lse = combine(po, pl, n_parts=None)          # arity=k or "chain" for the other orders
+    step = PreparedDecode(q, k, v, seqlens, chunk)    # fixed buffers: step() costs one C call
 """
 from __future__ import annotations
 
@@ -15,7 +16,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["decode", "partial", "combine", "TreeAttnError", "library_path", "load_library",
+__all__ = ["decode", "partial", "combine", "PreparedDecode", "stream_read", "TreeAttnError", "library_path", "load_library",
            "TA_OK", "TA_ERR_NULL", "TA_ERR_SHAPE", "TA_ERR_DTYPE", "TA_ERR_STRIDE", "TA_ERR_ARG",
            "TA_ERR_UNSUPPORTED", "TA_ERR_HIP", "TaTensor", "EXPORTS"]
 
@@ -166,6 +167,37 @@ def decode(q, k, v, seqlens=None, chunk: int = 2048, out=None, lse=None, stream=
     by = ctypes.byref
     _call(dev, stream, lambda s: lib.ta_decode(by(dq), by(dk), by(dv), sl, by(do), by(dl), int(chunk), s))
     return out, lse
+
+
+class PreparedDecode:
+    """ta_decode on fixed buffers, for loops that call it many times.
+
+    The descriptors of q, k, v, out and lse are built once; each call then costs
+    one C call. The buffers are read when the call runs, so the caller refills q,
+    k, v and seqlens in place between calls and reads out and lse after them.
+    The tensors must stay alive and keep their storage while the object is used.
+    """
+
+    def __init__(self, q, k, v, seqlens=None, chunk: int = 2048, out=None, lse=None):
+        import torch
+        dev = _same_device(q, k, v, out, lse)
+        B, Hq, d = q.shape
+        self.out = out if out is not None else torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+        self.lse = lse if lse is not None else torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        self._keep = (q, k, v, seqlens)
+        self._dev = dev
+        self._sl = _seqlens_ptr(seqlens, B, dev)
+        self._chunk = int(chunk)
+        self._d = [_desc(q), _desc(k), _desc(v), _desc(self.out), _desc(self.lse)]
+        self._lib = _lib or load_library()
+
+    def __call__(self, stream=None):
+        """Enqueues one decode step on `stream` (torch's current stream by default)."""
+        by = ctypes.byref
+        dq, dk, dv, do, dl = self._d
+        _call(self._dev, stream,
+              lambda s: self._lib.ta_decode(by(dq), by(dk), by(dv), self._sl, by(do), by(dl), self._chunk, s))
+        return self.out, self.lse
 
 
 def partial(q, k, v, seqlens=None, chunk: int = 2048, partial_o=None, partial_lse=None, stream=None):

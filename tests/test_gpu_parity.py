@@ -563,3 +563,21 @@ def test_grid_limits(B, Hq, Hkv, N, chunk):
     rows = rows[(rows >= 0) & (rows < B * Hq)]
     ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens, rows=rows)
     assert_close(out.reshape(-1, 64)[rows], lse.reshape(-1)[rows], ro, rl, "bf16", what=f"grid limits B={B} Hq={Hq}")
+
+
+def test_prepared_decode_reads_its_buffers_at_each_call():
+    a = W.random_decode(B=2, Hq=8, Hkv=2, N=900, d=128, dtype="bf16", seed=90, seqlens=[900, 333])
+    b = W.random_decode(B=2, Hq=8, Hkv=2, N=900, d=128, dtype="bf16", seed=91, seqlens=[500, 900])
+    q, k, v, sl = upload(a)
+    qb, kb, vb, slb = upload(b)
+    step = ta.PreparedDecode(q, k, v, sl, chunk=128)
+    out, lse = step()
+    ref = ta.decode(q, k, v, sl, chunk=128)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
+    # refill the same buffers in place: the next call sees the new contents
+    q.copy_(qb); k.copy_(kb); v.copy_(vb); sl.copy_(slb)
+    out, lse = step()
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(b.q, b.k, b.v, b.seqlens)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", what="prepared decode, refilled")
