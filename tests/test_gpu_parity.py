@@ -581,3 +581,39 @@ def test_prepared_decode_reads_its_buffers_at_each_call():
     torch.cuda.synchronize()
     ro, rl = oracle.decode(b.q, b.k, b.v, b.seqlens)
     assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", what="prepared decode, refilled")
+
+
+def _random_configs(n, seed):
+    rng = np.random.default_rng(seed)
+    cfgs = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        dtype = str(rng.choice(["bf16", "f32"]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        B = int(rng.integers(1, 9))
+        N = int(rng.integers(1, 6000))
+        chunk = int(rng.choice([1, 7, 16, 64, 128, 300, 512, 1024, 4096]))
+        if N // chunk > 3000:  # keep every case small enough for the oracle
+            chunk = max(chunk, N // 3000 + 1)
+        lens = [int(x) for x in rng.integers(0, N + 1, size=B)]
+        if rng.random() < 0.5:
+            lens = None
+        cfgs.append(dict(B=B, Hq=Hkv * G, Hkv=Hkv, N=N, d=d, dtype=dtype, chunk=chunk, seqlens=lens, seed=1000 + i))
+    return cfgs
+
+
+@pytest.mark.parametrize("cfg", _random_configs(48, 2024), ids=lambda c: f"B{c['B']}H{c['Hq']}/{c['Hkv']}N{c['N']}d{c['d']}{c['dtype']}c{c['chunk']}{'r' if c['seqlens'] else ''}")
+def test_random_shapes_against_oracle(cfg):
+    # a seeded mix of batch, GQA ratio, length, head dim, dtype, chunk and ragged
+    # lengths: small and large grids (4- and 8-wave workgroups), rotated chunk
+    # orders, multi-pass merges
+    c = dict(cfg)
+    chunk, sl, seed = c.pop("chunk"), c.pop("seqlens"), c.pop("seed")
+    inp = W.random_decode(**c, seed=seed, seqlens=sl)
+    log(f"random shape {cfg}")
+    q, k, v, sl_d = upload(inp)
+    out, lse = ta.decode(q, k, v, sl_d if sl is not None else None, chunk=chunk)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, c["dtype"], what=f"random {cfg}")
