@@ -12,19 +12,24 @@
 //    one row and a wave-wide load covers RG = 64 / SEGS consecutive rows (1 KB,
 //    fully coalesced). Each lane keeps its segment of q for every head of the group.
 //  - Per token, each lane forms the partial dot products of its segment with the G
-//    query segments (bf16 pairs through v_dot2_f32_bf16), and a DPP butterfly inside
-//    the SEGS-lane row sums them: the whole row group then knows the G logits.
+//    query segments (bf16 pairs through v_dot2_f32_bf16), and a DPP reduce-scatter
+//    inside the SEGS-lane row sums them by head: each lane ends with the logit of
+//    one head (lane mod G) for its tokens.
 //  - The running max, the rescale of the accumulators and the exponentials follow
 //    the page's merge operator, once per block of TPL tokens per lane, in base 2
-//    (exp(x) = 2^(x log2 e), the log2 e folded into the logit scale).
+//    (exp(x) = 2^(x log2 e), the log2 e folded into the logit scale); each lane
+//    exponentiates only its own head's logits.
 //  - V rows arrive in the same lane layout, so each lane accumulates the G heads
-//    for its own 16-byte slice of channels: no cross-lane traffic on the V side.
+//    for its own 16-byte slice of channels, each token's weight broadcast from a
+//    lane that holds its head.
 //  - The K/V rows of one block are in flight while the previous block is computed
 //    (two register buffers per lane). The GQA group shares every byte read: each
 //    K/V element is loaded once and used by all G heads.
 //  - Each wave walks the chunk in blocks of RG x TPL tokens, interleaved with the
-//    other waves. At the end the row groups of a wave, then the waves, are merged
-//    with the same operator (shuffles, then LDS) and the state is written.
+//    other waves (4 per workgroup, 8 when the grid has fewer workgroups than the
+//    device has compute units). At the end the row groups of a wave, then the
+//    waves, are merged with the same operator (shuffles, then LDS) and the state
+//    is written.
 #include <atomic>
 #include <type_traits>
 
