@@ -242,3 +242,22 @@ def test_last_error_is_per_call():
     assert rc != 0 and msg
     rc, msg = call_decode(good(B=0))
     assert rc == 0 and msg == ""
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # no fallback: with the shared library absent, loading raises and names the build step
+    import subprocess
+    import sys
+    code = (
+        "import softmax_tree_reduction_amd as ta\n"
+        f"ta._LIB_PATH = {str(tmp_path / 'libtreeattn.so')!r}\n"
+        "try:\n"
+        "    ta.load_library()\n"
+        "except RuntimeError as e:\n"
+        "    print('raised:', e)\n"
+        "else:\n"
+        "    print('loaded')\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert "raised:" in r.stdout and "build" in r.stdout, r.stdout + r.stderr
