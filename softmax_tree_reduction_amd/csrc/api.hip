@@ -225,7 +225,7 @@ int heads_per_wg(int64_t group) {
 
 ta::PartialParams partial_params(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const int32_t* seqlens,
                                  float* po, const int64_t po_st[3], float* pl, const int64_t pl_st[3],
-                                 const DecodeShape& s, int32_t chunk) {
+                                 const DecodeShape& s, int32_t chunk, bool empty_states) {
     ta::PartialParams p{};
     p.q = q->data;
     p.k = k->data;
@@ -251,6 +251,7 @@ ta::PartialParams partial_params(const ta_tensor* q, const ta_tensor* k, const t
     p.chunk = chunk;
     p.group = (int32_t)(s.Hq / s.Hkv);
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.d));
+    p.empty_states = empty_states ? 1 : 0;
     return p;
 }
 
@@ -347,7 +348,8 @@ int ta_partial(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const
     if (s.B == 0 || P == 0) return ok();
     const int gt = heads_per_wg(s.Hq / s.Hkv);
     ta::PartialParams p = partial_params(q, k, v, seqlens, static_cast<float*>(partial_o->data), partial_o->stride,
-                                         static_cast<float*>(partial_lse->data), partial_lse->stride, s, chunk);
+                                         static_cast<float*>(partial_lse->data), partial_lse->stride, s, chunk,
+                                         /*empty_states=*/true);
     hipError_t e = ta::launch_partial(p, s.dt, (int)s.d, gt, (int)s.B, (int)s.Hq, (int)P, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "partial kernel launch");
     return ok();
@@ -373,7 +375,11 @@ int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const 
     const int64_t po_st[3] = {s.Hq * P * s.d, P * s.d, s.d};
     const int64_t pl_st[3] = {s.Hq * P, P, 1};
     const int gt = heads_per_wg(s.Hq / s.Hkv);
-    ta::PartialParams p = partial_params(q, k, v, seqlens, po, po_st, pl, pl_st, s, chunk);
+    // With seqlens the merge reads only the chunks below ceil(n / chunk) of each row, so
+    // the chunks past a sequence's end need not be written; without, every chunk of the
+    // grid holds tokens except the one of an N = 0 cache, which the merge does read.
+    ta::PartialParams p = partial_params(q, k, v, seqlens, po, po_st, pl, pl_st, s, chunk,
+                                         /*empty_states=*/seqlens == nullptr);
     hipError_t e = ta::launch_partial(p, s.dt, (int)s.d, gt, (int)s.B, (int)s.Hq, (int)P, st);
     if (e != hipSuccess) return hip_fail(e, "partial kernel launch");
     const int64_t out_st[2] = {out->stride[0], out->stride[1]};

@@ -27,6 +27,11 @@ struct PartialParams {
     int32_t chunk;             // tokens per partial state
     int32_t group;             // query heads per KV head (Hq / Hkv)
     float scale_log2;          // log2(e) / sqrt(d)
+    // 1: a chunk past its sequence's end writes the empty state (0, -inf). 0: it
+    // writes nothing, for callers whose merge reads only the chunks that hold tokens.
+    int32_t empty_states;
+    // 1: the states are written with nontemporal stores (set by the launcher).
+    int32_t stream_states;
 };
 
 // Tree merge of partial states: one workgroup per (head, sequence, group of leaves).

@@ -115,6 +115,23 @@ __device__ __forceinline__ const uint4* row_ptr(const char* base, int64_t row, i
     return reinterpret_cast<const uint4*>(base + row * row_bytes);
 }
 
+// Writes one head's 16-byte slice of o and, from the lane of slice 0, its lse.
+// Nontemporal stores when `stream` is set: in grids of many rounds of workgroups
+// most states are written while other workgroups are still streaming K and V, and
+// ordinary write-back stores then cost the stream more than the bytes they carry.
+__device__ __forceinline__ void store_state(float* o_ptr, float* lse_ptr, float4 o, float lse, bool first,
+                                            bool stream) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    if (stream) {
+        const f32x4 v = {o.x, o.y, o.z, o.w};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(o_ptr));
+        if (first) __builtin_nontemporal_store(lse, lse_ptr);
+    } else {
+        *reinterpret_cast<float4*>(o_ptr) = o;
+        if (first) *lse_ptr = lse;
+    }
+}
+
 // The partial state of tokens [c0, c1) (c0 < c1) for the GT heads from h0, written to
 // po / pl (already offset to this sequence, head h0 and chunk).
 template <typename T, int D, int GT, int NW, int TPL, int NBUF>
@@ -353,8 +370,18 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
         } else {
             o = make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        *reinterpret_cast<float4*>(po + (int64_t)h * p.po_sh + 4 * c4) = o;
-        if (c4 == 0) pl[(int64_t)h * p.pl_sh] = lse;
+        store_state(po + (int64_t)h * p.po_sh + 4 * c4, pl + (int64_t)h * p.pl_sh, o, lse, c4 == 0,
+                    p.stream_states != 0);
+    }
+}
+
+// The empty state (o = 0, lse = -inf) of GT heads of one chunk.
+template <int D, int GT, int NW>
+__device__ __forceinline__ void write_empty(float* po, float* pl, const PartialParams& p) {
+    for (int i = threadIdx.x; i < GT * (D / 4); i += NW * kWave) {
+        const int h = i / (D / 4), c4 = i % (D / 4);
+        store_state(po + (int64_t)h * p.po_sh + 4 * c4, pl + (int64_t)h * p.pl_sh, make_float4(0.f, 0.f, 0.f, 0.f),
+                    -INFINITY, c4 == 0, p.stream_states != 0);
     }
 }
 
@@ -373,25 +400,30 @@ __global__ __launch_bounds__(NW * kWave) void partial_kernel(PartialParams p) {
     const int h0 = blockIdx.y * GT;
     const int b = blockIdx.z;
     const int g = h0 / p.group;
-    const int tid = threadIdx.x;
 
     int n = p.seqlens ? p.seqlens[b] : p.N;
     n = n < 0 ? 0 : (n > p.N ? p.N : n);
-    const int64_t c0 = (int64_t)chunk_idx * p.chunk;
-    const int64_t c1 = (c0 + p.chunk < (int64_t)n) ? c0 + p.chunk : (int64_t)n;
 
-    float* po = p.po + (int64_t)b * p.po_sb + (int64_t)h0 * p.po_sh + (int64_t)chunk_idx * p.po_sp;
-    float* pl = p.plse + (int64_t)b * p.pl_sb + (int64_t)h0 * p.pl_sh + (int64_t)chunk_idx * p.pl_sp;
-
-    if (c0 >= c1) {  // empty chunk: the identity state
-        for (int i = tid; i < GT * (D / 4); i += NW * kWave) {
-            const int h = i / (D / 4), c4 = i % (D / 4);
-            *reinterpret_cast<float4*>(po + (int64_t)h * p.po_sh + 4 * c4) = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (c4 == 0) pl[(int64_t)h * p.pl_sh] = -INFINITY;
-        }
+    // Chunks at or past nb hold no tokens. Their empty state (0, -inf) is written only
+    // if the caller reads it, and then by the workgroups that have work (chunk j also
+    // covers chunks j + nb, j + 2 nb, ...): an empty workgroup that stayed to store
+    // 2 KB would hold its compute-unit slot for a whole write latency. A row with no
+    // tokens at all has no such workgroup and writes its own.
+    const int64_t nb = ((int64_t)n + p.chunk - 1) / p.chunk;
+    float* po_row = p.po + (int64_t)b * p.po_sb + (int64_t)h0 * p.po_sh;
+    float* pl_row = p.plse + (int64_t)b * p.pl_sb + (int64_t)h0 * p.pl_sh;
+    if (chunk_idx >= nb) {
+        if (p.empty_states && nb == 0)
+            write_empty<D, GT, NW>(po_row + (int64_t)chunk_idx * p.po_sp, pl_row + (int64_t)chunk_idx * p.pl_sp, p);
         return;
     }
-    chunk_state<T, D, GT, NW, TPL, NBUF>(p, b, h0, g, c0, c1, po, pl);
+    const int64_t c0 = (int64_t)chunk_idx * p.chunk;
+    const int64_t c1 = (c0 + p.chunk < (int64_t)n) ? c0 + p.chunk : (int64_t)n;
+    chunk_state<T, D, GT, NW, TPL, NBUF>(p, b, h0, g, c0, c1, po_row + (int64_t)chunk_idx * p.po_sp,
+                                         pl_row + (int64_t)chunk_idx * p.pl_sp);
+    if (p.empty_states)
+        for (int64_t c = chunk_idx + nb; c < (int64_t)gridDim.x; c += nb)
+            write_empty<D, GT, NW>(po_row + c * p.po_sp, pl_row + c * p.pl_sp, p);
 }
 
 
@@ -421,10 +453,17 @@ hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hip
     constexpr int NW = TA_PARTIAL_WAVES, NWS = TA_PARTIAL_WAVES_SMALL;
     dim3 grid(n_chunks, Hq / GT, B);
     const int64_t wgs = (int64_t)n_chunks * (Hq / GT) * B;
-    if (NWS != NW && wgs < device_cus())
-        hipLaunchKernelGGL((partial_kernel<T, D, GT, NWS, TPL, NBUF>), grid, dim3(NWS * kWave), 0, stream, p);
+    const int cus = device_cus();
+    // Nontemporal state stores pay off when the grid is more than about two rounds of
+    // resident workgroups (8 per compute unit); with fewer, the states are written at
+    // the tail of the stream, and write-back stores are as cheap and leave them in L2
+    // for the merge.
+    PartialParams q = p;
+    q.stream_states = wgs > 8 * (int64_t)cus ? 1 : 0;
+    if (NWS != NW && wgs < cus)
+        hipLaunchKernelGGL((partial_kernel<T, D, GT, NWS, TPL, NBUF>), grid, dim3(NWS * kWave), 0, stream, q);
     else
-        hipLaunchKernelGGL((partial_kernel<T, D, GT, NW, TPL, NBUF>), grid, dim3(NW * kWave), 0, stream, p);
+        hipLaunchKernelGGL((partial_kernel<T, D, GT, NW, TPL, NBUF>), grid, dim3(NW * kWave), 0, stream, q);
     return hipGetLastError();
 }
 

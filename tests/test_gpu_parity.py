@@ -105,6 +105,36 @@ def test_partial_states_match_oracle_windows():
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,chunk,seqlens", [
+    # 48 workgroups: write-back state stores
+    (3, 8, 2, 2400, 128, 300, [2400, 700, 0]),
+    # 8192 workgroups (more than 8 per compute unit): nontemporal state stores
+    (4, 32, 8, 4096, 128, 16, [4096, 9, 0, 17]),
+    (8, 8, 8, 2048, 64, 8, [2048, 1, 0, 9, 1000, 8, 2047, 17]),
+])
+def test_partial_writes_every_slot(B, Hq, Hkv, N, d, chunk, seqlens):
+    # Chunks past a sequence's end hold the empty state (0, -inf), written by the
+    # row's non-empty chunks (a row with one or two of them writes hundreds), or by
+    # the chunk itself when the row has no tokens. The buffers start as NaN, so a
+    # slot nobody wrote fails.
+    inp = W.random_decode(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype="bf16", seed=B * 100 + chunk, seqlens=seqlens)
+    P = -(-N // chunk)
+    log(f"partial slots: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} chunk={chunk} P={P} workgroups={P * B * Hq // min(Hq // Hkv, 8)}")
+    q, k, v, sl = upload(inp)
+    po = torch.full((B, Hq, P, d), float("nan"), dtype=torch.float32, device="cuda")
+    pl = torch.full((B, Hq, P), float("nan"), dtype=torch.float32, device="cuda")
+    ta.partial(q, k, v, sl, chunk=chunk, partial_o=po, partial_lse=pl)
+    torch.cuda.synchronize()
+    po, pl = po.cpu().numpy(), pl.cpu().numpy()
+    for b, n in enumerate(seqlens):
+        nb = -(-n // chunk)
+        assert np.all(po[b, :, nb:] == 0.0) and np.all(np.isneginf(pl[b, :, nb:])), f"row {b}: empty slots"
+        assert np.all(np.isfinite(po[b, :, :nb])) and np.all(np.isfinite(pl[b, :, :nb])), f"row {b}: unwritten slot"
+    for i in range(max(-(-n // chunk) for n in seqlens)):
+        ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens, t_begin=i * chunk, t_end=(i + 1) * chunk)
+        assert_close(po[:, :, i], pl[:, :, i], ro, rl, "bf16", what=f"partial {i}")
+
+
 @pytest.mark.parametrize("n_parts", [1, 3, 5, 7, 64, 128, 200, 1000, 20000])
 @pytest.mark.parametrize("d", [128, 64])
 def test_combine_against_oracle(n_parts, d):
