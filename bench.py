@@ -156,6 +156,8 @@ def main() -> int:
     ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk")
     ap.add_argument("--min-rotation-bytes", type=float, default=2 * 2**30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="device time of streaming reads run before the warmup steps (0: none)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--mode", choices=["step", "partial", "copy", "combine"], default="step",
                     help="step: the benchmark line (default); partial: only the timed partial-kernel launches "
@@ -250,11 +252,38 @@ def main() -> int:
     print(f"bench: parity on {len(rows)} sampled rows ok (max|out-oracle| {perr:.2e}, lse rel {lerr:.2e})",
           file=sys.stderr, flush=True)
 
+    # ---- settle, then the practical read ceiling: a plain streaming read of 1 GiB (several
+    # times the caches). The device reaches its steady speed only after some tens of ms
+    # of sustained load, so the probe runs for --settle-ms of device time before anything
+    # is timed (0 skips the settling); the ceiling is then timed over 20 more reads.
+    probe = torch.empty(2**30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    settled_ms, settle_reads = 0.0, 0
+    while True:
+        ev0.record(stream)
+        for _ in range(3 if settle_reads == 0 else 50):
+            ta.stream_read(probe, sink)
+            settle_reads += 1
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        settled_ms += ev0.elapsed_time(ev1)
+        if settled_ms >= args.settle_ms:
+            break
+    ev0.record(stream)
+    for _ in range(20):
+        ta.stream_read(probe, sink)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ceiling = probe.numel() / (ev0.elapsed_time(ev1) / 20 * 1e-3) / 1e9
+    del probe
+    print(f"bench: settled {settled_ms:.0f} ms ({settle_reads} reads of 1 GiB), read ceiling {ceiling:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
     # ---- whole step: ta_decode (partial kernel + tree merge)
     for i in range(args.warmup):
         ta.decode(q, ks[i % copies], vs[i % copies], sl, chunk=chunk, out=out, lse=lse)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
@@ -322,19 +351,6 @@ def main() -> int:
     ms_combine = ev0.elapsed_time(ev1) / args.steps
     del graph
 
-    # ---- practical read ceiling: a plain streaming read of 1 GiB (several times the caches)
-    probe = torch.empty(2**30, dtype=torch.uint8, device=dev)
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    for _ in range(3):
-        ta.stream_read(probe, sink)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(20):
-        ta.stream_read(probe, sink)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ceiling = probe.numel() / (ev0.elapsed_time(ev1) / 20 * 1e-3) / 1e9
-    del probe
 
     partial_bytes = step_bytes - wl.B * wl.Hq * (wl.d + 1) * 4  # K, V and q; out/lse belong to the merge
     achieved = partial_bytes / (ms_partial * 1e-3) / 1e9
@@ -361,6 +377,8 @@ def main() -> int:
         "us_per_step_warm": round(ms_warm * 1e3, 2),
         "read_ceiling": {"value": round(ceiling, 1), "unit": "GB/s", "kernel": "ta_stream_read",
                          "bytes_per_launch": 2**30, "step_pct_of_ceiling": round(100 * gbs / ceiling, 2)},
+        "settle": {"ms": round(settled_ms, 1), "kernel": "ta_stream_read", "launches": settle_reads,
+                   "note": "streaming reads before the warmup steps, so the timed steps run at the device's steady speed"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
