@@ -108,7 +108,7 @@ def test_partial_states_match_oracle_windows():
 @pytest.mark.parametrize("B,Hq,Hkv,N,d,chunk,seqlens", [
     # 48 workgroups: write-back state stores
     (3, 8, 2, 2400, 128, 300, [2400, 700, 0]),
-    # 8192 workgroups (more than 8 per compute unit): nontemporal state stores
+    # 8192 and 16384 workgroups (more than 8 per compute unit): nontemporal state stores
     (4, 32, 8, 4096, 128, 16, [4096, 9, 0, 17]),
     (8, 8, 8, 2048, 64, 8, [2048, 1, 0, 9, 1000, 8, 2047, 17]),
 ])
@@ -133,6 +133,34 @@ def test_partial_writes_every_slot(B, Hq, Hkv, N, d, chunk, seqlens):
     for i in range(max(-(-n // chunk) for n in seqlens)):
         ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens, t_begin=i * chunk, t_end=(i + 1) * chunk)
         assert_close(po[:, :, i], pl[:, :, i], ro, rl, "bf16", what=f"partial {i}")
+
+
+@pytest.mark.parametrize("B,seqlens", [
+    (2, [1000, 0]),                                   # 1024 workgroups: write-back state stores
+    (4, [4096, 1, 0, 1000]),                          # 2048 workgroups: write-back state stores
+    (8, [4096, 1, 0, 1000, 64, 65, 4095, 2000]),      # 4096 workgroups: nontemporal state stores
+])
+def test_decode_never_reads_chunks_past_the_end(B, seqlens):
+    # With seqlens, ta_decode leaves the states of chunks past a sequence's end
+    # unwritten: the merge must not read them. A first call on the same stream and
+    # shapes, at full length, fills every slot of the workspace with a state whose
+    # lse (about 30, from keys scaled by 8) dwarfs any real one here (1 to 9) and
+    # whose o is 1024: one stale slot read would pull that row's output to 1024.
+    Hq, Hkv, N, d, chunk = 32, 8, 4096, 128, 64
+    log(f"stale workspace: B={B} N={N} chunk={chunk} seqlens={seqlens}")
+    inp = W.random_decode(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype="bf16", seed=B + 7, seqlens=seqlens)
+    q, k, v, sl = upload(inp)
+    gen = torch.Generator(device="cuda").manual_seed(B)
+    big_k = (torch.randn(k.shape, generator=gen, device="cuda") * 8).to(torch.bfloat16)
+    big_v = torch.full_like(v, 1024.0)
+    full = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    out, lse = ta.decode(q, big_k, big_v, full, chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.allclose(out, torch.full_like(out, 1024.0)) and (lse > 20).all(), "poisoning call"
+    out, lse = ta.decode(q, k, v, sl, chunk=chunk)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "bf16", what="after a poisoned workspace")
 
 
 @pytest.mark.parametrize("n_parts", [1, 3, 5, 7, 64, 128, 200, 1000, 20000])
