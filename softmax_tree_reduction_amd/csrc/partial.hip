@@ -30,6 +30,9 @@
 //    device has compute units). At the end the row groups of a wave, then the
 //    waves, are merged with the same operator (shuffles, then LDS) and the state
 //    is written.
+//  - A chunk past its sequence's end does no work. Its empty state, when the
+//    caller reads it, is written by the row's non-empty workgroups. Grids of many
+//    rounds of workgroups write the states with nontemporal stores.
 #include <atomic>
 #include <type_traits>
 
@@ -455,9 +458,9 @@ hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hip
     const int64_t wgs = (int64_t)n_chunks * (Hq / GT) * B;
     const int cus = device_cus();
     // Nontemporal state stores pay off when the grid is more than about two rounds of
-    // resident workgroups (8 per compute unit); with fewer, the states are written at
-    // the tail of the stream, and write-back stores are as cheap and leave them in L2
-    // for the merge.
+    // resident workgroups (8 per compute unit). With fewer, most states are written
+    // near the tail of the stream, where write-back stores cost no more and leave the
+    // states in L2 for the merge.
     PartialParams q = p;
     q.stream_states = wgs > 8 * (int64_t)cus ? 1 : 0;
     if (NWS != NW && wgs < cus)
