@@ -351,7 +351,6 @@ def main() -> int:
     ms_combine = ev0.elapsed_time(ev1) / args.steps
     del graph
 
-
     partial_bytes = step_bytes - wl.B * wl.Hq * (wl.d + 1) * 4  # K, V and q; out/lse belong to the merge
     achieved = partial_bytes / (ms_partial * 1e-3) / 1e9
     traffic = measured_traffic(wl.name)
