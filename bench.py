@@ -96,6 +96,35 @@ def cpu_baseline(inp, wl, budget_s: float):
                               "ms_per_step": round(one * 1e3, 1)}}
 
 
+def settle_and_read_ceiling(ta, torch, dev, stream, settle_ms: float):
+    """Streams a 1 GiB buffer (several times the caches) with ta_stream_read for
+    `settle_ms` of device time, then times 20 more reads: the practical read ceiling.
+    The device reaches its steady speed only after some tens of ms of sustained load,
+    so this runs before anything is timed. Returns (settled ms, reads, GB/s)."""
+    probe = torch.empty(2**30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    settled_ms, reads = 0.0, 0
+    while True:
+        ev0.record(stream)
+        for _ in range(3 if reads == 0 else 50):
+            ta.stream_read(probe, sink)
+            reads += 1
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        settled_ms += ev0.elapsed_time(ev1)
+        if settled_ms >= settle_ms:
+            break
+    ev0.record(stream)
+    for _ in range(20):
+        ta.stream_read(probe, sink)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ceiling = probe.numel() / (ev0.elapsed_time(ev1) / 20 * 1e-3) / 1e9
+    del probe
+    return settled_ms, reads, ceiling
+
+
 def bench_combine(args, dev) -> int:
     """ta_combine (or ta_combine_k with --arity K) alone on the combine workload:
     one GPU's share of a 64-shard merge."""
@@ -127,6 +156,7 @@ def bench_combine(args, dev) -> int:
         print(f"bench: combine parity failed ({err}, {lerr})", file=sys.stderr)
         return 1
     stream = torch.cuda.current_stream(dev)
+    settled_ms, _, _ = settle_and_read_ceiling(ta, torch, dev, stream, args.settle_ms)
     for i in range(args.warmup):
         ta.combine(pos[i % copies], pls[i % copies], out=out, lse=lse, arity=args.arity)
     torch.cuda.synchronize()
@@ -137,10 +167,33 @@ def bench_combine(args, dev) -> int:
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    # the same calls replayed from a captured graph: device time without the binding's
+    # per-call host cost (which is about as long as the kernel)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        ta.combine(pos[0], pls[0], out=out, lse=lse, arity=args.arity)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(args.steps):
+            ta.combine(pos[i % copies], pls[i % copies], out=out, lse=lse, arity=args.arity)
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_graph = ev0.elapsed_time(ev1) / args.steps
+    del graph
     kernel = {None: "ta_combine", "chain": "ta_combine_chain"}.get(args.arity, "ta_combine_k")
     print(json.dumps({"mode": "combine", "workload": cw.name, "arity": args.arity or 2,
                       "kernel": kernel, "us_per_call": round(ms * 1e3, 2),
+                      "us_per_call_graph": round(ms_graph * 1e3, 2),
                       "bytes_per_call": nbytes, "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                      "GB_per_s_graph": round(nbytes / (ms_graph * 1e-3) / 1e9, 1),
+                      "settle_ms": round(settled_ms, 1),
                       "rows": cw.B * cw.H, "n_parts": cw.n_parts, "copies": copies,
                       "max_abs_out_err": err, "max_rel_lse_err": lerr}))
     return 0
@@ -252,31 +305,9 @@ def main() -> int:
     print(f"bench: parity on {len(rows)} sampled rows ok (max|out-oracle| {perr:.2e}, lse rel {lerr:.2e})",
           file=sys.stderr, flush=True)
 
-    # ---- settle, then the practical read ceiling: a plain streaming read of 1 GiB (several
-    # times the caches). The device reaches its steady speed only after some tens of ms
-    # of sustained load, so the probe runs for --settle-ms of device time before anything
-    # is timed (0 skips the settling); the ceiling is then timed over 20 more reads.
-    probe = torch.empty(2**30, dtype=torch.uint8, device=dev)
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    # ---- settle, then the practical read ceiling (before anything is timed)
+    settled_ms, settle_reads, ceiling = settle_and_read_ceiling(ta, torch, dev, stream, args.settle_ms)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    settled_ms, settle_reads = 0.0, 0
-    while True:
-        ev0.record(stream)
-        for _ in range(3 if settle_reads == 0 else 50):
-            ta.stream_read(probe, sink)
-            settle_reads += 1
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        settled_ms += ev0.elapsed_time(ev1)
-        if settled_ms >= args.settle_ms:
-            break
-    ev0.record(stream)
-    for _ in range(20):
-        ta.stream_read(probe, sink)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ceiling = probe.numel() / (ev0.elapsed_time(ev1) / 20 * 1e-3) / 1e9
-    del probe
     print(f"bench: settled {settled_ms:.0f} ms ({settle_reads} reads of 1 GiB), read ceiling {ceiling:.0f} GB/s",
           file=sys.stderr, flush=True)
 
