@@ -348,6 +348,44 @@ def test_bitwise_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+def test_concurrent_threads_and_streams():
+    # Serving code may call ta_decode from several host threads, each on a stream of
+    # its own. Every (device, stream) pair has its own workspace, grown when a call
+    # needs more; each thread cycles through shapes of different sizes, and every
+    # result must be the one a single stream gives, bit for bit.
+    import threading
+    cases = []
+    for i, (N, chunk, sl) in enumerate([(20000, 1024, [20000, 13001]), (9000, 256, [9000, 1]),
+                                        (30000, 2048, [29999, 30000])]):
+        inp = W.random_decode(B=2, Hq=32, Hkv=8, N=N, d=128, dtype="bf16", seed=40 + i, seqlens=sl)
+        q, k, v, s = upload(inp)
+        cases.append((q, k, v, s, chunk, ta.decode(q, k, v, s, chunk=chunk)))
+    torch.cuda.synchronize()
+    log(f"concurrent: 3 threads x 20 calls over {len(cases)} shapes")
+    errors = []
+
+    def worker(tid):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                for it in range(20):
+                    q, k, v, s, chunk, (ref_o, ref_l) = cases[(tid + it) % len(cases)]
+                    out, lse = ta.decode(q, k, v, s, chunk=chunk, stream=stream)
+                    stream.synchronize()
+                    if not (torch.equal(out, ref_o) and torch.equal(lse, ref_l)):
+                        errors.append(f"thread {tid}, call {it}: result differs")
+        except Exception as e:  # reported below, in the main thread
+            errors.append(f"thread {tid}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(3)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
+
+
 def test_seqlens_none_and_lse_none_paths():
     inp = W.random_decode(B=1, Hq=8, Hkv=2, N=1000, d=64, dtype="bf16", seed=14)
     q, k, v, _ = upload(inp)
