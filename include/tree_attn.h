@@ -189,6 +189,26 @@ int ta_partial(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v,
  */
 int ta_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * ta_suggest_chunk - a chunk for ta_decode or ta_partial that gives the partial
+ * kernel about one workgroup per compute unit, which measured fastest on
+ * batches whose sequences all hold n tokens: the largest power of two, at
+ * least 64 and at most n, for which
+ *     batch x head groups x ceil(n / chunk) >= compute units,
+ * where head groups = q_heads / (the largest of 8, 4, 2, 1 dividing
+ * q_heads / kv_heads). In ragged batches the short sequences leave such a grid
+ * partly idle, and a smaller chunk does better. The chunk is the merge tree's
+ * leaf, so the choice changes the rounding of the result, never its meaning.
+ *
+ *   batch, q_heads, kv_heads, n   as in ta_decode (n: tokens per sequence)
+ *   compute_units                 > 0, or 0 for the current device's count
+ *
+ * Returns the chunk (>= 64), or TA_ERR_ARG for a size below 1 or q_heads not a
+ * multiple of kv_heads, or TA_ERR_HIP when the device cannot be queried, with
+ * the message in ta_last_error. Launches nothing.
+ */
+int32_t ta_suggest_chunk(int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t n, int32_t compute_units);
+
 /* Message for the last non-zero return on this thread ("" if none). Never NULL. */
 const char* ta_last_error(void);
 

@@ -9,6 +9,7 @@ fallback path.
     po, pl   = partial(q, k, v, seqlens=None, chunk=2048)
     out, lse = combine(po, pl, n_parts=None)          # arity=k or "chain" for the other orders
     step = PreparedDecode(q, k, v, seqlens, chunk)    # fixed buffers: step() costs one C call
+    chunk = suggest_chunk(B, Hq, Hkv, N)              # about one workgroup per compute unit
 """
 from __future__ import annotations
 
@@ -16,7 +17,8 @@ import ctypes
 import os
 import threading
 
-__all__ = ["decode", "partial", "combine", "PreparedDecode", "stream_read", "TreeAttnError", "library_path", "load_library",
+__all__ = ["decode", "partial", "combine", "PreparedDecode", "stream_read", "suggest_chunk", "TreeAttnError",
+           "library_path", "load_library",
            "TA_OK", "TA_ERR_NULL", "TA_ERR_SHAPE", "TA_ERR_DTYPE", "TA_ERR_STRIDE", "TA_ERR_ARG",
            "TA_ERR_UNSUPPORTED", "TA_ERR_HIP", "TaTensor", "EXPORTS"]
 
@@ -24,7 +26,7 @@ TA_OK, TA_ERR_NULL, TA_ERR_SHAPE, TA_ERR_DTYPE, TA_ERR_STRIDE, TA_ERR_ARG, TA_ER
     0, -1, -2, -3, -4, -5, -6, -7
 TA_F32, TA_BF16 = 0, 1
 EXPORTS = ("ta_decode", "ta_combine", "ta_combine_k", "ta_combine_chain", "ta_partial", "ta_stream_read",
-           "ta_last_error", "ta_version")
+           "ta_suggest_chunk", "ta_last_error", "ta_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtreeattn.so")
@@ -74,6 +76,9 @@ def load_library():
             lib.ta_combine_k.argtypes = [P, P, i32, i32, P, P, vp]
             lib.ta_combine_chain.argtypes = [P, P, i32, P, P, vp]
             lib.ta_stream_read.argtypes = [vp, ctypes.c_int64, vp, vp]
+            i64 = ctypes.c_int64
+            lib.ta_suggest_chunk.argtypes = [i64, i64, i64, i64, i32]
+            lib.ta_suggest_chunk.restype = ctypes.c_int32
             for f in (lib.ta_decode, lib.ta_partial, lib.ta_combine, lib.ta_combine_k, lib.ta_combine_chain,
                       lib.ta_stream_read):
                 f.restype = ctypes.c_int
@@ -257,3 +262,13 @@ def stream_read(buf, sink, stream=None):
     nbytes = buf.numel() * buf.element_size()
     _call(dev, stream, lambda s: lib.ta_stream_read(ctypes.c_void_p(buf.data_ptr()), ctypes.c_int64(nbytes),
                                                     ctypes.c_void_p(sink.data_ptr()), s))
+
+
+def suggest_chunk(batch: int, q_heads: int, kv_heads: int, n: int, compute_units: int = 0) -> int:
+    """ta_suggest_chunk: the largest power-of-two chunk (>= 64, <= n) that still gives
+    the partial kernel at least one workgroup per compute unit; compute_units 0 asks
+    the current device. Meant for batches whose sequences all hold n tokens."""
+    lib = _lib or load_library()
+    c = lib.ta_suggest_chunk(int(batch), int(q_heads), int(kv_heads), int(n), int(compute_units))
+    _check(c if c < 0 else TA_OK)
+    return int(c)

@@ -334,6 +334,27 @@ int run_combine(const float* po, const int64_t po_st[3], const float* pl, const 
 
 extern "C" {
 
+int32_t ta_suggest_chunk(int64_t batch, int64_t q_heads, int64_t kv_heads, int64_t n, int32_t compute_units) {
+    if (batch < 1 || q_heads < 1 || kv_heads < 1 || n < 1)
+        return fail(TA_ERR_ARG, "batch, q_heads, kv_heads and n must be >= 1");
+    if (q_heads % kv_heads != 0)
+        return fail(TA_ERR_ARG, "q_heads (%lld) must be a multiple of kv_heads (%lld)", (long long)q_heads,
+                    (long long)kv_heads);
+    int cus = compute_units;
+    if (cus <= 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e, "compute-unit count");
+        if (cus <= 0) return fail(TA_ERR_HIP, "the device reports %d compute units", cus);
+    }
+    const int64_t rows = batch * (q_heads / heads_per_wg(q_heads / kv_heads));  // workgroups per chunk index
+    int64_t chunk = 64;
+    while (2 * chunk <= n && rows * ((n + 2 * chunk - 1) / (2 * chunk)) >= cus) chunk *= 2;
+    ok();
+    return (int32_t)chunk;
+}
+
 int ta_version(void) { return 1; }
 
 const char* ta_last_error(void) { return g_last_error.c_str(); }

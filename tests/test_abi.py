@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
     lib = ta.load_library()
     names = declared_functions()
     assert {"ta_decode", "ta_combine", "ta_combine_k", "ta_combine_chain", "ta_partial", "ta_stream_read",
-            "ta_last_error", "ta_version"} <= names
+            "ta_suggest_chunk", "ta_last_error", "ta_version"} <= names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/ but not exported"
     assert set(ta.EXPORTS) == names
@@ -204,6 +204,31 @@ def test_stream_read_validation():
     rc, msg = call(FAKE + 8, 16, FAKE)
     assert rc == ta.TA_ERR_ARG and "aligned" in msg
     assert call(FAKE, 0, FAKE) == (ta.TA_OK, "")
+
+
+def test_suggest_chunk():
+    # the chunks that measured fastest for one 8B-GQA sequence (32 query heads, 8 KV
+    # heads: 8 head groups) on 256 compute units give one workgroup per CU each
+    for n, want in [(8192, 256), (32768, 1024), (131072, 4096), (1 << 20, 32768)]:
+        assert ta.suggest_chunk(1, 32, 8, n, compute_units=256) == want
+    assert ta.suggest_chunk(4, 32, 8, 524288, compute_units=256) == 65536
+    # the defining property over a grid of shapes: the largest power of two (>= 64,
+    # <= n unless n < 64) whose grid still has a workgroup per compute unit
+    for B in (1, 3, 32):
+        for Hq, Hkv in ((32, 8), (8, 8), (12, 4), (5, 1)):
+            g = next(x for x in (8, 4, 2, 1) if (Hq // Hkv) % x == 0)
+            rows = B * Hq // g
+            for n in (1, 63, 64, 100, 4096, 100000, 1 << 20):
+                for cus in (1, 80, 256, 304):
+                    c = ta.suggest_chunk(B, Hq, Hkv, n, compute_units=cus)
+                    assert c >= 64 and c & (c - 1) == 0
+                    wgs = lambda ch: rows * -(-n // ch)
+                    assert c == 64 or (c <= n and wgs(c) >= cus)
+                    assert 2 * c > n or wgs(2 * c) < cus
+    for args in ((0, 32, 8, 1000), (1, 0, 8, 1000), (1, 32, 0, 1000), (1, 32, 8, 0), (1, 30, 8, 1000)):
+        with pytest.raises(ta.TreeAttnError) as e:
+            ta.suggest_chunk(*args, compute_units=256)
+        assert e.value.code == ta.TA_ERR_ARG
 
 
 def test_merge_group_limit_is_refused_before_launch():

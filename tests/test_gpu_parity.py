@@ -713,3 +713,9 @@ def test_random_shapes_against_oracle(cfg):
     torch.cuda.synchronize()
     ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
     assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, c["dtype"], what=f"random {cfg}")
+
+
+def test_suggest_chunk_reads_the_device():
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for n in (8192, 131072, 1 << 20):
+        assert ta.suggest_chunk(1, 32, 8, n) == ta.suggest_chunk(1, 32, 8, n, compute_units=cus)
