@@ -345,6 +345,23 @@ def main() -> int:
     print(f"bench: {args.steps} steps, {ms_step * 1e3:.1f} us/step (host wall {wall / args.steps * 1e6:.1f} us/step)",
           file=sys.stderr, flush=True)
 
+    # ---- the same step at the chunk ta_suggest_chunk gives (reported apart, not `value`)
+    alt_chunk = ta.suggest_chunk(wl.B, wl.Hq, wl.Hkv, wl.N)
+    alt = None
+    if alt_chunk != chunk:
+        for i in range(args.warmup):
+            ta.decode(q, ks[i % copies], vs[i % copies], sl, chunk=alt_chunk, out=out, lse=lse)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            ta.decode(q, ks[i % copies], vs[i % copies], sl, chunk=alt_chunk, out=out, lse=lse)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_alt = ev0.elapsed_time(ev1) / args.steps
+        alt = {"chunk": alt_chunk, "us_per_step": round(ms_alt * 1e3, 2),
+               "GB_per_s": round(step_bytes / (ms_alt * 1e-3) / 1e9, 2),
+               "note": "same workload and timing, at the chunk ta_suggest_chunk returns; not value"}
+
     # ---- dominant kernel alone: ta_partial over the same rotation
     po = torch.empty(wl.B, wl.Hq, P, wl.d, dtype=torch.float32, device=dev)
     pl = torch.empty(wl.B, wl.Hq, P, dtype=torch.float32, device=dev)
@@ -405,6 +422,7 @@ def main() -> int:
         "us_per_step_dist": {"median": round(pct(0.5), 2), "p10": round(pct(0.1), 2), "p90": round(pct(0.9), 2),
                              "note": "separate pass, an event after every step (adds the events' own cost)"},
         "us_per_step_warm": round(ms_warm * 1e3, 2),
+        "suggested_chunk": alt,
         "read_ceiling": {"value": round(ceiling, 1), "unit": "GB/s", "kernel": "ta_stream_read",
                          "bytes_per_launch": 2**30, "step_pct_of_ceiling": round(100 * gbs / ceiling, 2)},
         "settle": {"ms": round(settled_ms, 1), "kernel": "ta_stream_read", "launches": settle_reads,
