@@ -135,6 +135,26 @@ def test_partial_writes_every_slot(B, Hq, Hkv, N, d, chunk, seqlens):
         assert_close(po[:, :, i], pl[:, :, i], ro, rl, "bf16", what=f"partial {i}")
 
 
+@pytest.mark.parametrize("chunk", [64, 16])
+def test_partial_clamps_out_of_range_seqlens(chunk):
+    # lengths below 0 or above N act as 0 and N: every slot, the empty ones included,
+    # holds what the clamped lengths give (chunk 16: 8192 workgroups, nontemporal stores)
+    N = 4096 if chunk == 16 else 1000
+    inp = W.random_decode(B=4, Hq=32, Hkv=8, N=N, d=128, dtype="bf16", seed=chunk, seqlens=[N, 0, 3, N])
+    q, k, v, _ = upload(inp)
+    P = -(-N // chunk)
+    res = []
+    for lens in ([N + 1000, -5, 3, 2**31 - 1], [N, 0, 3, N]):
+        po = torch.full((4, 32, P, 128), float("nan"), dtype=torch.float32, device="cuda")
+        pl = torch.full((4, 32, P), float("nan"), dtype=torch.float32, device="cuda")
+        ta.partial(q, k, v, torch.tensor(lens, dtype=torch.int32, device="cuda"), chunk=chunk,
+                   partial_o=po, partial_lse=pl)
+        res.append((po, pl))
+    torch.cuda.synchronize()
+    assert not torch.isnan(res[1][0]).any() and not torch.isnan(res[1][1]).any()
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
 @pytest.mark.parametrize("B,seqlens", [
     (2, [1000, 0]),                                   # 1024 workgroups: write-back state stores
     (4, [4096, 1, 0, 1000]),                          # 2048 workgroups: write-back state stores
