@@ -76,7 +76,7 @@ enum {
     TA_ERR_DTYPE = -3,        /* unsupported or mismatched dtype */
     TA_ERR_STRIDE = -4,       /* d not contiguous, or a row not 16-byte aligned */
     TA_ERR_ARG = -5,          /* chunk < 1, n_parts out of range, ... */
-    TA_ERR_UNSUPPORTED = -6,  /* a head dimension or size this build has no kernel for */
+    TA_ERR_UNSUPPORTED = -6,  /* a head dimension or size the library has no kernel for */
     TA_ERR_HIP = -7           /* the HIP runtime returned an error */
 };
 
