@@ -58,6 +58,11 @@
 namespace ta {
 namespace {
 
+// Most chunks one workgroup of the several-chunks kernel streams (its LDS holds one
+// set of wave states per chunk until the end: 8 x 4 waves x GT x D floats, 128 KiB
+// at GT = 8, d = 128).
+constexpr int kMaxChunksPerWG = 8;
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <typename T>
@@ -137,18 +142,27 @@ __device__ __forceinline__ void store_state(float* o_ptr, float* lse_ptr, float4
 
 // The partial state of tokens [c0, c1) (c0 < c1) for the GT heads from h0, written to
 // po / pl (already offset to this sequence, head h0 and chunk).
-template <typename T, int D, int GT, int NW, int TPL, int NBUF>
+// MULTI: [c0, c1) is instead nc (<= kMaxChunksPerWG) consecutive whole chunks of
+// p.chunk tokens, each a whole number of rounds of NW blocks. Each wave walks all of
+// them in one stream; at the end of each chunk it leaves its part of that chunk's
+// state in LDS and streams on, with no barrier. After the last chunk the workgroup
+// merges the waves' parts of every chunk and writes chunk j's state to po + j * p.po_sp,
+// pl + j * p.pl_sp. Every wave takes the same blocks of each chunk, in the same order,
+// as it would for that chunk alone, and the merges are the same, so the states are
+// the same bits.
+template <typename T, int D, int GT, int NW, int TPL, int NBUF, bool MULTI = false>
 __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h0, int g, int64_t c0, int64_t c1,
-                                            float* po, float* pl) {
+                                            float* po, float* pl, int nc = 1) {
     constexpr int E = Storage<T>::kElems;  // elements per 16-byte segment
     constexpr int SEGS = D / E;            // lanes per row
     constexpr int RG = kWave / SEGS;       // rows per wave-wide load
     constexpr int BT = RG * TPL;           // tokens per wave block
     static_assert(SEGS >= 8 && SEGS <= 32 && RG * SEGS == kWave, "row layout");
 
-    __shared__ float sm_acc[NW][GT][D];
-    __shared__ float sm_m[NW][GT];
-    __shared__ float sm_l[NW][GT];
+    constexpr int SLOTS = MULTI ? kMaxChunksPerWG : 1;  // chunks whose wave states wait in LDS
+    __shared__ float sm_acc[SLOTS][NW][GT][D];
+    __shared__ float sm_m[SLOTS][NW][GT];
+    __shared__ float sm_l[SLOTS][NW][GT];
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -279,11 +293,96 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
         }
     };
 
+    // The end of a chunk, in two halves. park: this wave merges its row groups (lanes
+    // that hold the same channels) with the page's operator, leaves the result in LDS
+    // slot `slot` and starts a fresh state; no other wave is waited for. finish: after
+    // one barrier, the waves' states of each slot are merged and written, normalised,
+    // to (po_j, pl_j).
+    auto park = [&](int slot) {
+        // every head's running max and sum, in every lane of the row
+        float m[GT], l[GT];
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+            m[h] = bcast_head(m_own, h);
+            l[h] = bcast_head(l_own, h);
+        }
+
+        // merge the row groups of this wave (lanes that hold the same channels)
+#pragma unroll
+        for (int off = SEGS; off < kWave; off <<= 1) {
+#pragma unroll
+            for (int h = 0; h < GT; ++h) {
+                const float mo = __shfl_xor(m[h], off, kWave);
+                const float lo = __shfl_xor(l[h], off, kWave);
+                const Rescale r = merge_factors(m[h], mo);
+                l[h] = r.a * l[h] + r.b * lo;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float ao = __shfl_xor(acc[h][e], off, kWave);
+                    acc[h][e] = r.a * acc[h][e] + r.b * ao;
+                }
+                m[h] = r.m;
+            }
+        }
+
+        // and leave it in LDS for the merge across the waves
+        if (rg == 0) {
+#pragma unroll
+            for (int h = 0; h < GT; ++h) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) sm_acc[slot][wave][h][seg * E + e] = acc[h][e];
+                if (seg == 0) {
+                    sm_m[slot][wave][h] = m[h];
+                    sm_l[slot][wave][h] = l[h];
+                }
+            }
+        }
+        m_own = -INFINITY;
+        l_own = 0.0f;
+#pragma unroll
+        for (int h = 0; h < GT; ++h)
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[h][e] = 0.0f;
+    };
+    auto finish = [&](int slot, float* po_j, float* pl_j) {
+        for (int i = tid; i < GT * (D / 4); i += NW * kWave) {
+            const int h = i / (D / 4), c4 = i % (D / 4);
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[slot][w][h]);
+            const float ref = (M == -INFINITY) ? 0.0f : M;
+            float L = 0.0f;
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float f = exp2_fast(sm_m[slot][w][h] - ref);
+                L += f * sm_l[slot][w][h];
+                o.x += f * sm_acc[slot][w][h][4 * c4 + 0];
+                o.y += f * sm_acc[slot][w][h][4 * c4 + 1];
+                o.z += f * sm_acc[slot][w][h][4 * c4 + 2];
+                o.w += f * sm_acc[slot][w][h][4 * c4 + 3];
+            }
+            float lse = -INFINITY;
+            if (L > 0.0f) {
+                const float inv = 1.0f / L;
+                o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
+                lse = (M + __log2f(L)) * kLn2;
+            } else {
+                o = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            store_state(po_j + (int64_t)h * p.po_sh + 4 * c4, pl_j + (int64_t)h * p.pl_sh, o, lse, c4 == 0,
+                        p.stream_states != 0);
+        }
+    };
+
     // Full blocks, interleaved over the waves, through a ring of NBUF register
     // buffers: blocks blk+NW, ..., blk+(NBUF-1)NW are in flight while block blk is
     // computed. Then the partial last block, if any, by the wave it falls to.
     const int64_t nfull = (c1 - c0) / BT;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int64_t per_chunk = MULTI ? nfull / nc / NW : 0;  // blocks of one chunk per wave
+    int64_t done = 0;
+    int cur = 0;
     {
         uint4 kb[NBUF][TPL], vb[NBUF][TPL];
         int64_t blk = wave_u;
@@ -300,82 +399,26 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
                     compute_block(std::false_type{}, c0 + blk * BT, kb[s], vb[s]);
                     blk += NW;
                     more = blk < nfull;
+                    if constexpr (MULTI) {
+                        if (++done == per_chunk) {  // this wave's last block of chunk cur
+                            park(cur);
+                            done = 0;
+                            ++cur;
+                        }
+                    }
                 }
             }
         }
-        if (c0 + nfull * BT < c1 && nfull % NW == wave_u) {
-            load_tail(c0 + nfull * BT, kb[0], vb[0]);
-            compute_block(std::true_type{}, c0 + nfull * BT, kb[0], vb[0]);
-        }
-    }
-
-    // every head's running max and sum, in every lane of the row
-    float m[GT], l[GT];
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-        m[h] = bcast_head(m_own, h);
-        l[h] = bcast_head(l_own, h);
-    }
-
-    // merge the row groups of this wave (lanes that hold the same channels)
-#pragma unroll
-    for (int off = SEGS; off < kWave; off <<= 1) {
-#pragma unroll
-        for (int h = 0; h < GT; ++h) {
-            const float mo = __shfl_xor(m[h], off, kWave);
-            const float lo = __shfl_xor(l[h], off, kWave);
-            const Rescale r = merge_factors(m[h], mo);
-            l[h] = r.a * l[h] + r.b * lo;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float ao = __shfl_xor(acc[h][e], off, kWave);
-                acc[h][e] = r.a * acc[h][e] + r.b * ao;
-            }
-            m[h] = r.m;
-        }
-    }
-
-    // then the waves, through LDS
-    if (rg == 0) {
-#pragma unroll
-        for (int h = 0; h < GT; ++h) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) sm_acc[wave][h][seg * E + e] = acc[h][e];
-            if (seg == 0) {
-                sm_m[wave][h] = m[h];
-                sm_l[wave][h] = l[h];
+        if constexpr (!MULTI) {
+            if (c0 + nfull * BT < c1 && nfull % NW == wave_u) {
+                load_tail(c0 + nfull * BT, kb[0], vb[0]);
+                compute_block(std::true_type{}, c0 + nfull * BT, kb[0], vb[0]);
             }
         }
     }
+    if constexpr (!MULTI) park(0);
     __syncthreads();
-    for (int i = tid; i < GT * (D / 4); i += NW * kWave) {
-        const int h = i / (D / 4), c4 = i % (D / 4);
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
-        const float ref = (M == -INFINITY) ? 0.0f : M;
-        float L = 0.0f;
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float f = exp2_fast(sm_m[w][h] - ref);
-            L += f * sm_l[w][h];
-            o.x += f * sm_acc[w][h][4 * c4 + 0];
-            o.y += f * sm_acc[w][h][4 * c4 + 1];
-            o.z += f * sm_acc[w][h][4 * c4 + 2];
-            o.w += f * sm_acc[w][h][4 * c4 + 3];
-        }
-        float lse = -INFINITY;
-        if (L > 0.0f) {
-            const float inv = 1.0f / L;
-            o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
-            lse = (M + __log2f(L)) * kLn2;
-        } else {
-            o = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        store_state(po + (int64_t)h * p.po_sh + 4 * c4, pl + (int64_t)h * p.pl_sh, o, lse, c4 == 0,
-                    p.stream_states != 0);
-    }
+    for (int j = 0; j < (MULTI ? nc : 1); ++j) finish(j, po + (int64_t)j * p.po_sp, pl + (int64_t)j * p.pl_sp);
 }
 
 // The empty state (o = 0, lse = -inf) of GT heads of one chunk.
@@ -430,6 +473,23 @@ __global__ __launch_bounds__(NW * kWave) void partial_kernel(PartialParams p) {
 }
 
 
+// Rows of equal length whose chunks are all whole: workgroup x of a row streams the
+// cpw chunks cpw * x, ..., cpw * x + cpw - 1 in one pass and writes one state per
+// chunk (a row whose chunk count is no multiple of cpw would give its last
+// workgroup fewer; the launcher does not ask for that).
+template <typename T, int D, int GT, int NW, int TPL, int NBUF>
+__global__ __launch_bounds__(NW * kWave) void partial_kernel_multi(PartialParams p, int n_chunks, int cpw) {
+    const int first = blockIdx.x * cpw;
+    const int nc = cpw < n_chunks - first ? cpw : n_chunks - first;
+    const int h0 = blockIdx.y * GT;
+    const int b = blockIdx.z;
+    const int g = h0 / p.group;
+    float* po = p.po + (int64_t)b * p.po_sb + (int64_t)h0 * p.po_sh + (int64_t)first * p.po_sp;
+    float* pl = p.plse + (int64_t)b * p.pl_sb + (int64_t)h0 * p.pl_sh + (int64_t)first * p.pl_sp;
+    const int64_t c0 = (int64_t)first * p.chunk;
+    chunk_state<T, D, GT, NW, TPL, NBUF, true>(p, b, h0, g, c0, c0 + (int64_t)nc * p.chunk, po, pl, nc);
+}
+
 // Compute units of the current device (cached per device).
 int device_cus() {
     static std::atomic<int> cache[64];
@@ -463,6 +523,22 @@ hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hip
     // states in L2 for the merge.
     PartialParams q = p;
     q.stream_states = wgs > 8 * (int64_t)cus ? 1 : 0;
+    // A grid of exactly 4 to 8 rounds of CUs streams 1.3-2.6% faster as one
+    // workgroup per CU, each taking that many consecutive chunks in one stream
+    // (measured at 4 rounds on 128k, 1M and 2 x 512k tokens, and at 8 on 1M).
+    // With 2 or 3 rounds it measured even or slower, and with a fraction of a round
+    // the CUs that get two workgroups make it much slower. It needs rows of equal
+    // length (no seqlens) cut into whole chunks, each a whole number of rounds of NW
+    // blocks, so that every wave reaches each chunk's end at the same step.
+    constexpr int BT = (kWave / (D / Storage<T>::kElems)) * TPL;
+    const int64_t cpw = cus > 0 && wgs % cus == 0 ? wgs / cus : 0;
+    if (!p.seqlens && p.N > 0 && p.N % p.chunk == 0 && p.chunk % (BT * NW) == 0 && cpw >= 4 &&
+        cpw <= kMaxChunksPerWG && n_chunks % cpw == 0) {  // exactly one workgroup per CU
+        dim3 gm((unsigned)((n_chunks + cpw - 1) / cpw), Hq / GT, B);
+        hipLaunchKernelGGL((partial_kernel_multi<T, D, GT, NW, TPL, NBUF>), gm, dim3(NW * kWave), 0, stream, q,
+                           n_chunks, (int)cpw);
+        return hipGetLastError();
+    }
     if (NWS != NW && wgs < cus)
         hipLaunchKernelGGL((partial_kernel<T, D, GT, NWS, TPL, NBUF>), grid, dim3(NWS * kWave), 0, stream, q);
     else

@@ -739,3 +739,37 @@ def test_suggest_chunk_reads_the_device():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for n in (8192, 131072, 1 << 20):
         assert ta.suggest_chunk(1, 32, 8, n) == ta.suggest_chunk(1, 32, 8, n, compute_units=cus)
+
+
+@pytest.mark.parametrize("B,per_cu,dtype,d", [
+    (1, 4, "bf16", 128), (1, 8, "bf16", 128), (2, 4, "bf16", 128), (1, 4, "bf16", 64), (1, 5, "f32", 128),
+    (2, 4, "f32", 64), (1, 2, "bf16", 128), (3, 6, "bf16", 128),
+])
+def test_several_chunks_per_workgroup_are_bitwise_the_per_chunk_states(B, per_cu, dtype, d):
+    # Without seqlens, rows of whole chunks in a grid of exactly 4 to 8 rounds of CUs
+    # go to the kernel that streams several chunks per workgroup; full-length seqlens
+    # take the per-chunk kernel over the same tokens. Every state, and ta_decode's
+    # result, must be the same bits. 2 rounds, and B = 3 at 6 rounds (64 chunks per
+    # row, no multiple of 6), stay on the per-chunk kernel.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    Hq, Hkv, chunk = 32, 8, 2048
+    if (per_cu * cus) % (8 * B):
+        pytest.skip(f"{per_cu} rounds of {cus} CUs is no whole number of chunks per row")
+    n_chunks = per_cu * cus // (8 * B)  # 8 head groups of 4 query heads
+    N = n_chunks * chunk
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cuda").manual_seed(B * 100 + per_cu * 10 + d)
+    q = torch.randn(B, Hq, d, generator=gen, device="cuda").to(tdt)
+    k = torch.randn(B, Hkv, N, d, generator=gen, device="cuda").to(tdt)
+    v = torch.randn(B, Hkv, N, d, generator=gen, device="cuda").to(tdt)
+    full = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    log(f"chunks per workgroup: B={B} {dtype} d={d} N={N} ({n_chunks} chunks per row, {per_cu} rounds of {cus} CUs)")
+    a = ta.partial(q, k, v, None, chunk=chunk)
+    b = ta.partial(q, k, v, full, chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a[0]).all() and torch.isfinite(a[1]).all()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    c = ta.decode(q, k, v, None, chunk=chunk)
+    e = ta.decode(q, k, v, full, chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(c[0], e[0]) and torch.equal(c[1], e[1])
