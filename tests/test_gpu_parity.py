@@ -741,21 +741,23 @@ def test_suggest_chunk_reads_the_device():
         assert ta.suggest_chunk(1, 32, 8, n) == ta.suggest_chunk(1, 32, 8, n, compute_units=cus)
 
 
-@pytest.mark.parametrize("B,per_cu,dtype,d", [
-    (1, 4, "bf16", 128), (1, 8, "bf16", 128), (2, 4, "bf16", 128), (1, 4, "bf16", 64), (1, 5, "f32", 128),
-    (2, 4, "f32", 64), (1, 2, "bf16", 128), (3, 6, "bf16", 128),
+@pytest.mark.parametrize("B,per_cu,dtype,d,Hkv", [
+    (1, 4, "bf16", 128, 8), (1, 8, "bf16", 128, 8), (2, 4, "bf16", 128, 8), (1, 4, "bf16", 64, 8),
+    (1, 5, "f32", 128, 8), (2, 4, "f32", 64, 8), (1, 2, "bf16", 128, 8), (3, 6, "bf16", 128, 8),
+    (1, 8, "bf16", 128, 4), (1, 4, "f32", 128, 4),  # 8 query heads per workgroup: the largest instance
 ])
-def test_several_chunks_per_workgroup_are_bitwise_the_per_chunk_states(B, per_cu, dtype, d):
+def test_several_chunks_per_workgroup_are_bitwise_the_per_chunk_states(B, per_cu, dtype, d, Hkv):
     # Without seqlens, rows of whole chunks in a grid of exactly 4 to 8 rounds of CUs
     # go to the kernel that streams several chunks per workgroup; full-length seqlens
     # take the per-chunk kernel over the same tokens. Every state, and ta_decode's
     # result, must be the same bits. 2 rounds, and B = 3 at 6 rounds (64 chunks per
     # row, no multiple of 6), stay on the per-chunk kernel.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    Hq, Hkv, chunk = 32, 8, 2048
-    if (per_cu * cus) % (8 * B):
+    Hq, chunk = 32, 2048
+    groups = Hq // min(8, Hq // Hkv)  # workgroups per chunk of a sequence (Hq / Hkv is 4 or 8 here)
+    if (per_cu * cus) % (groups * B):
         pytest.skip(f"{per_cu} rounds of {cus} CUs is no whole number of chunks per row")
-    n_chunks = per_cu * cus // (8 * B)  # 8 head groups of 4 query heads
+    n_chunks = per_cu * cus // (groups * B)
     N = n_chunks * chunk
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     gen = torch.Generator(device="cuda").manual_seed(B * 100 + per_cu * 10 + d)
@@ -763,7 +765,7 @@ def test_several_chunks_per_workgroup_are_bitwise_the_per_chunk_states(B, per_cu
     k = torch.randn(B, Hkv, N, d, generator=gen, device="cuda").to(tdt)
     v = torch.randn(B, Hkv, N, d, generator=gen, device="cuda").to(tdt)
     full = torch.full((B,), N, dtype=torch.int32, device="cuda")
-    log(f"chunks per workgroup: B={B} {dtype} d={d} N={N} ({n_chunks} chunks per row, {per_cu} rounds of {cus} CUs)")
+    log(f"chunks per workgroup: B={B} Hkv={Hkv} {dtype} d={d} N={N} ({n_chunks} chunks per row, {per_cu} rounds of {cus} CUs)")
     a = ta.partial(q, k, v, None, chunk=chunk)
     b = ta.partial(q, k, v, full, chunk=chunk)
     torch.cuda.synchronize()
