@@ -58,10 +58,11 @@
 namespace ta {
 namespace {
 
-// Most chunks one workgroup of the several-chunks kernel streams (its LDS holds one
-// set of wave states per chunk until the end: 8 x 4 waves x GT x D floats, 128 KiB
-// at GT = 8, d = 128).
-constexpr int kMaxChunksPerWG = 8;
+// Most chunks one workgroup of the several-chunks kernel streams. Its LDS holds one
+// set of wave states per chunk until the end, slots x 4 waves x GT x D floats: 128 KiB
+// at 16 slots with GT = 4 or 8 slots with GT = 8 (d = 128), of the 160 KiB a CU has.
+template <int GT>
+constexpr int max_chunks_per_wg() { return GT <= 4 ? 16 : 8; }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -142,7 +143,7 @@ __device__ __forceinline__ void store_state(float* o_ptr, float* lse_ptr, float4
 
 // The partial state of tokens [c0, c1) (c0 < c1) for the GT heads from h0, written to
 // po / pl (already offset to this sequence, head h0 and chunk).
-// MULTI: [c0, c1) is instead nc (<= kMaxChunksPerWG) consecutive whole chunks of
+// MULTI: [c0, c1) is instead nc (<= max_chunks_per_wg) consecutive whole chunks of
 // p.chunk tokens, each a whole number of rounds of NW blocks. Each wave walks all of
 // them in one stream; at the end of each chunk it leaves its part of that chunk's
 // state in LDS and streams on, with no barrier. After the last chunk the workgroup
@@ -159,7 +160,7 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
     constexpr int BT = RG * TPL;           // tokens per wave block
     static_assert(SEGS >= 8 && SEGS <= 32 && RG * SEGS == kWave, "row layout");
 
-    constexpr int SLOTS = MULTI ? kMaxChunksPerWG : 1;  // chunks whose wave states wait in LDS
+    constexpr int SLOTS = MULTI ? max_chunks_per_wg<GT>() : 1;  // chunks whose wave states wait in LDS
     __shared__ float sm_acc[SLOTS][NW][GT][D];
     __shared__ float sm_m[SLOTS][NW][GT];
     __shared__ float sm_l[SLOTS][NW][GT];
@@ -523,9 +524,10 @@ hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hip
     // states in L2 for the merge.
     PartialParams q = p;
     q.stream_states = wgs > 8 * (int64_t)cus ? 1 : 0;
-    // A grid of exactly 4 to 8 rounds of CUs streams 1.3-2.6% faster as one
-    // workgroup per CU, each taking that many consecutive chunks in one stream
-    // (measured at 4 rounds on 128k, 1M and 2 x 512k tokens, and at 8 on 1M).
+    // A grid of exactly 4 to 16 rounds of CUs (8 with GT = 8) streams 0.7-2.8% faster
+    // as one workgroup per CU, each taking that many consecutive chunks in one stream
+    // (measured at 4 rounds on 128k, 1M and 2 x 512k tokens, 8 on 1M, 16 on 1M and
+    // 4 x 512k).
     // With 2 or 3 rounds it measured even or slower, and with a fraction of a round
     // the CUs that get two workgroups make it much slower. It needs rows of equal
     // length (no seqlens) cut into whole chunks, each a whole number of rounds of NW
@@ -533,7 +535,7 @@ hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hip
     constexpr int BT = (kWave / (D / Storage<T>::kElems)) * TPL;
     const int64_t cpw = cus > 0 && wgs % cus == 0 ? wgs / cus : 0;
     if (!p.seqlens && p.N > 0 && p.N % p.chunk == 0 && p.chunk % (BT * NW) == 0 && cpw >= 4 &&
-        cpw <= kMaxChunksPerWG && n_chunks % cpw == 0) {  // exactly one workgroup per CU
+        cpw <= max_chunks_per_wg<GT>() && n_chunks % cpw == 0) {  // exactly one workgroup per CU
         dim3 gm((unsigned)((n_chunks + cpw - 1) / cpw), Hq / GT, B);
         hipLaunchKernelGGL((partial_kernel_multi<T, D, GT, NW, TPL, NBUF>), gm, dim3(NW * kWave), 0, stream, q,
                            n_chunks, (int)cpw);
