@@ -30,6 +30,26 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
 #endif
 }
 
+// The value lane (lane ^ off) holds, for off a power of two below 64. Offsets 16
+// and 32 go through gfx950's row and half swaps (v_permlane16_swap_b32,
+// v_permlane32_swap_b32), which stay in the VALU: given two copies of x, the first
+// result holds every even row's (lower half's) values in both rows (halves) of a
+// pair and the second every odd row's (upper half's), so each lane takes its
+// partner's from the other parity. Smaller offsets use the ordinary shuffle.
+__device__ __forceinline__ float xor_lanes(float x, int off) {
+    const unsigned lane = __lane_id();
+    const unsigned u = __float_as_uint(x);
+    if (off == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __uint_as_float(((lane >> 4) & 1u) ? r[0] : r[1]);
+    }
+    if (off == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __uint_as_float((lane >> 5) ? r[0] : r[1]);
+    }
+    return __shfl_xor(x, off, 64);
+}
+
 // 2^x on the hardware exponential unit; 2^-inf = 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -313,13 +313,13 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
         for (int off = SEGS; off < kWave; off <<= 1) {
 #pragma unroll
             for (int h = 0; h < GT; ++h) {
-                const float mo = __shfl_xor(m[h], off, kWave);
-                const float lo = __shfl_xor(l[h], off, kWave);
+                const float mo = xor_lanes(m[h], off);
+                const float lo = xor_lanes(l[h], off);
                 const Rescale r = merge_factors(m[h], mo);
                 l[h] = r.a * l[h] + r.b * lo;
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float ao = __shfl_xor(acc[h][e], off, kWave);
+                    const float ao = xor_lanes(acc[h][e], off);
                     acc[h][e] = r.a * acc[h][e] + r.b * ao;
                 }
                 m[h] = r.m;
@@ -510,6 +510,22 @@ int device_cus() {
 // each busy one streams with only the bytes its waves keep in flight: such grids
 // get more waves per workgroup (measured 16-20% faster at 64 and 128 workgroups,
 // even at 256, slower from 512 on).
+// Workgroups of the per-chunk kernel one CU holds at once (limited by its registers
+// and LDS), from the runtime; 0 if it cannot say.
+template <typename T, int D, int GT, int NW, int TPL, int NBUF>
+int per_chunk_capacity() {
+    static std::atomic<int> cache{0};
+    const int v = cache.load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, partial_kernel<T, D, GT, NW, TPL, NBUF>, NW * kWave, 0) !=
+            hipSuccess ||
+        n <= 0)
+        return 0;
+    cache.store(n, std::memory_order_relaxed);
+    return n;
+}
+
 template <typename T, int D, int GT>
 hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hipStream_t stream) {
     constexpr int TPL = GT >= 8 ? (TA_PARTIAL_TPL > 4 ? 4 : TA_PARTIAL_TPL) : TA_PARTIAL_TPL;
@@ -524,18 +540,20 @@ hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hip
     // states in L2 for the merge.
     PartialParams q = p;
     q.stream_states = wgs > 8 * (int64_t)cus ? 1 : 0;
-    // A grid of exactly 4 to 16 rounds of CUs (8 with GT = 8) streams 0.7-2.8% faster
-    // as one workgroup per CU, each taking that many consecutive chunks in one stream
-    // (measured at 4 rounds on 128k, 1M and 2 x 512k tokens, 8 on 1M, 16 on 1M and
-    // 4 x 512k).
-    // With 2 or 3 rounds it measured even or slower, and with a fraction of a round
-    // the CUs that get two workgroups make it much slower. It needs rows of equal
-    // length (no seqlens) cut into whole chunks, each a whole number of rounds of NW
-    // blocks, so that every wave reaches each chunk's end at the same step.
+    // A grid of a whole number k (2 to 16, 8 with GT = 8) of workgroups per CU streams
+    // 0.7-3.2% faster as one workgroup per CU taking k consecutive chunks in one
+    // stream (measured with k = 2, 4, 8 and 16 on 128k to 4 x 512k tokens) -- unless
+    // the per-chunk grid itself fills whole rounds of resident workgroups (k a
+    // multiple of the workgroups a CU holds: 3 for the bf16 d = 128 kernel), which
+    // then stream at least as well (measured with k = 3 and 6). With a fraction of a
+    // workgroup per CU the CUs that get two make it much slower. It needs rows of
+    // equal length (no seqlens) cut into whole chunks, each a whole number of rounds
+    // of NW blocks, so that every wave reaches each chunk's end at the same step.
     constexpr int BT = (kWave / (D / Storage<T>::kElems)) * TPL;
     const int64_t cpw = cus > 0 && wgs % cus == 0 ? wgs / cus : 0;
-    if (!p.seqlens && p.N > 0 && p.N % p.chunk == 0 && p.chunk % (BT * NW) == 0 && cpw >= 4 &&
-        cpw <= max_chunks_per_wg<GT>() && n_chunks % cpw == 0) {  // exactly one workgroup per CU
+    const int cap = cpw >= 2 ? per_chunk_capacity<T, D, GT, NW, TPL, NBUF>() : 0;
+    if (!p.seqlens && p.N > 0 && p.N % p.chunk == 0 && p.chunk % (BT * NW) == 0 && cpw >= 2 &&
+        cpw <= max_chunks_per_wg<GT>() && n_chunks % cpw == 0 && cap > 0 && cpw % cap != 0) {
         dim3 gm((unsigned)((n_chunks + cpw - 1) / cpw), Hq / GT, B);
         hipLaunchKernelGGL((partial_kernel_multi<T, D, GT, NW, TPL, NBUF>), gm, dim3(NW * kWave), 0, stream, q,
                            n_chunks, (int)cpw);
