@@ -443,7 +443,7 @@ def main() -> int:
                                  "sha256_first_mib": {n: hashlib.sha256(a.reshape(-1).view(np.uint8)[:2**20].tobytes())
                                                       .hexdigest()[:16] for n, a in (("q", inp.q), ("k", inp.k), ("v", inp.v))}}},
         "kernels_us": {"partial": round(ms_partial * 1e3, 2), "combine": round(ms_combine * 1e3, 2)},
-        "roofline": {"kernel": "partial_kernel", "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+        "roofline": {"kernel": "ta_partial (partial_kernel, or partial_kernel_multi when its grid takes several chunks per workgroup)", "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": partial_bytes,
                      "frac_of_read_ceiling": round(achieved / ceiling, 4)},
