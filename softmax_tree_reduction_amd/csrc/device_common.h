@@ -30,25 +30,6 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
 #endif
 }
 
-// The value lane (lane ^ off) holds, for off a power of two below 64. Offsets 16
-// and 32 go through gfx950's row and half swaps (v_permlane16_swap_b32,
-// v_permlane32_swap_b32), which stay in the VALU: given two copies of x, the first
-// result holds every even row's (lower half's) values in both rows (halves) of a
-// pair and the second every odd row's (upper half's), so each lane takes its
-// partner's from the other parity. Smaller offsets use the ordinary shuffle.
-__device__ __forceinline__ float xor_lanes(float x, int off) {
-    const unsigned lane = __lane_id();
-    const unsigned u = __float_as_uint(x);
-    if (off == 16) {
-        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-        return __uint_as_float(((lane >> 4) & 1u) ? r[0] : r[1]);
-    }
-    if (off == 32) {
-        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        return __uint_as_float((lane >> 5) ? r[0] : r[1]);
-    }
-    return __shfl_xor(x, off, 64);
-}
 
 // 2^x on the hardware exponential unit; 2^-inf = 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -70,7 +51,7 @@ __device__ __forceinline__ float dpp_mov(float x) {
 // gives lane i the value of lane (i - N) mod 16, so lanes whose bit 2 is clear read
 // lane i + 4 through row_ror:12 and the others lane i - 4 through row_ror:4, each
 // half written under its bank mask (a bank is 4 lanes); K = 8: row_ror:8 inside
-// the 16-lane row; K = 16: across rows through ds_bpermute.
+// the 16-lane row; K = 16: across rows through v_permlane16_swap (see xor_lanes).
 template <int K>
 __device__ __forceinline__ float lane_xor(float x) {
     if constexpr (K == 1) {
@@ -85,8 +66,28 @@ __device__ __forceinline__ float lane_xor(float x) {
         return dpp_mov<0x128>(x);
     } else {
         static_assert(K == 16, "lane_xor");
-        return __shfl_xor(x, 16, kWave);
+        const unsigned u = __float_as_uint(x);
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __uint_as_float(((__lane_id() >> 4) & 1u) ? r[0] : r[1]);
     }
+}
+
+// The value lane (lane ^ off) holds, for off in {8, 16, 32} without any LDS traffic:
+// 8 through DPP row_ror:8 inside the 16-lane row, 16 and 32 through gfx950's row
+// and half swaps (v_permlane16_swap_b32, v_permlane32_swap_b32). Given two copies
+// of x, a swap's first result holds every even row's (lower half's) values in both
+// rows (halves) of a pair and the second every odd row's (upper half's), so each
+// lane takes its partner's from the other parity. Other offsets use the ordinary
+// shuffle.
+__device__ __forceinline__ float xor_lanes(float x, int off) {
+    if (off == 8) return lane_xor<8>(x);
+    if (off == 16) return lane_xor<16>(x);
+    if (off == 32) {
+        const unsigned u = __float_as_uint(x);
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __uint_as_float((__lane_id() >> 5) ? r[0] : r[1]);
+    }
+    return __shfl_xor(x, off, 64);
 }
 
 // Lane K of each aligned group of L lanes (L in {8, 16, 32}, K < 8), for every lane
