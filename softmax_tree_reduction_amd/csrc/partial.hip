@@ -64,6 +64,9 @@ namespace {
 template <int GT>
 constexpr int max_chunks_per_wg() { return GT <= 4 ? 16 : 8; }
 
+// Shortest stream (tokens per workgroup) for which a workgroup takes several chunks.
+constexpr int64_t kMultiMinTokens = 8192;
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <typename T>
@@ -379,17 +382,49 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
     // Full blocks, interleaved over the waves, through a ring of NBUF register
     // buffers: blocks blk+NW, ..., blk+(NBUF-1)NW are in flight while block blk is
     // computed. Then the partial last block, if any, by the wave it falls to.
+    // The loop runs in two phases. While every prefetch of a turn of the ring lies
+    // inside the range, the loads are issued unconditionally, so the compiler's
+    // count of loads in flight stays exact and block blk waits for its own loads
+    // only. A prefetch under a branch would merge that count with the branch's
+    // not-taken side, and each block would then also wait for the prefetch just
+    // issued, leaving the memory latency of every turn exposed. The last turns
+    // (at most 2 NBUF - 1 blocks per wave) take the branch.
+    // The several-chunks kernel for bf16 with d = 128 runs the branch form
+    // throughout: there the workgroup streams 8192 tokens or more alone on its CU,
+    // and that form measured 0.7-1.5% faster (1M and 4 x 512k tokens), while the
+    // steady form measured faster everywhere else (the per-chunk kernel, and
+    // d = 64, whose blocks take twice the arithmetic per byte).
     const int64_t nfull = (c1 - c0) / BT;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int64_t per_chunk = MULTI ? nfull / nc / NW : 0;  // blocks of one chunk per wave
     int64_t done = 0;
     int cur = 0;
+    auto after_block = [&]() {
+        if constexpr (MULTI) {
+            if (++done == per_chunk) {  // this wave's last block of chunk cur
+                park(cur);
+                done = 0;
+                ++cur;
+            }
+        }
+    };
     {
         uint4 kb[NBUF][TPL], vb[NBUF][TPL];
         int64_t blk = wave_u;
 #pragma unroll
         for (int s = 0; s < NBUF - 1; ++s)
             if (blk + s * NW < nfull) load_full(c0 + (blk + s * NW) * BT, kb[s], vb[s]);
+        // steady turns: the last prefetch of the turn, block blk + (2 NBUF - 2) NW, exists
+        constexpr bool kSteady = !MULTI || !(std::is_same<T, uint16_t>::value && D == 128);
+        while (kSteady && blk + (2 * NBUF - 2) * NW < nfull) {
+#pragma unroll
+            for (int s = 0; s < NBUF; ++s) {
+                load_full(c0 + (blk + (NBUF - 1) * NW) * BT, kb[(s + NBUF - 1) % NBUF], vb[(s + NBUF - 1) % NBUF]);
+                compute_block(std::false_type{}, c0 + blk * BT, kb[s], vb[s]);
+                blk += NW;
+                after_block();
+            }
+        }
         bool more = blk < nfull;
         while (more) {
 #pragma unroll
@@ -400,13 +435,7 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
                     compute_block(std::false_type{}, c0 + blk * BT, kb[s], vb[s]);
                     blk += NW;
                     more = blk < nfull;
-                    if constexpr (MULTI) {
-                        if (++done == per_chunk) {  // this wave's last block of chunk cur
-                            park(cur);
-                            done = 0;
-                            ++cur;
-                        }
-                    }
+                    after_block();
                 }
             }
         }
@@ -541,11 +570,13 @@ hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hip
     PartialParams q = p;
     q.stream_states = wgs > 8 * (int64_t)cus ? 1 : 0;
     // A grid of a whole number k (2 to 16, 8 with GT = 8) of workgroups per CU streams
-    // 0.7-3.2% faster as one workgroup per CU taking k consecutive chunks in one
-    // stream (measured with k = 2, 4, 8 and 16 on 128k to 4 x 512k tokens) -- unless
-    // the per-chunk grid itself fills whole rounds of resident workgroups (k a
-    // multiple of the workgroups a CU holds: 3 for the bf16 d = 128 kernel), which
-    // then stream at least as well (measured with k = 3 and 6). With a fraction of a
+    // 0.4-2.2% faster as one workgroup per CU taking k consecutive chunks in one
+    // stream, when that stream is at least 8192 tokens long (measured with k = 2 to
+    // 16 on 256k to 4 x 512k tokens) -- unless the per-chunk grid itself fills whole
+    // rounds of resident workgroups (k a multiple of the workgroups a CU holds: 3 for
+    // the bf16 d = 128 kernel), which then stream at least as well (measured with
+    // k = 3 and 6). Over shorter streams (4096 tokens per CU at 128k) the per-chunk
+    // grid was 1-10% faster, the more so the more chunks. With a fraction of a
     // workgroup per CU the CUs that get two make it much slower. It needs rows of
     // equal length (no seqlens) cut into whole chunks, each a whole number of rounds
     // of NW blocks, so that every wave reaches each chunk's end at the same step.
@@ -553,7 +584,8 @@ hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hip
     const int64_t cpw = cus > 0 && wgs % cus == 0 ? wgs / cus : 0;
     const int cap = cpw >= 2 ? per_chunk_capacity<T, D, GT, NW, TPL, NBUF>() : 0;
     if (!p.seqlens && p.N > 0 && p.N % p.chunk == 0 && p.chunk % (BT * NW) == 0 && cpw >= 2 &&
-        cpw <= max_chunks_per_wg<GT>() && n_chunks % cpw == 0 && cap > 0 && cpw % cap != 0) {
+        cpw <= max_chunks_per_wg<GT>() && n_chunks % cpw == 0 && cpw * p.chunk >= kMultiMinTokens && cap > 0 &&
+        cpw % cap != 0) {
         dim3 gm((unsigned)((n_chunks + cpw - 1) / cpw), Hq / GT, B);
         hipLaunchKernelGGL((partial_kernel_multi<T, D, GT, NW, TPL, NBUF>), gm, dim3(NW * kWave), 0, stream, q,
                            n_chunks, (int)cpw);
