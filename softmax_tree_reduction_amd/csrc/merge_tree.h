@@ -108,18 +108,19 @@ __device__ __forceinline__ MState reduce_leaves(const Leaves<R>& lv, MergeSmem<D
     }
     MState st = leaf[0];
     // remaining levels across slots: slot s merges slot s + t when s is a multiple of 2t.
-    // Levels whose two slots share a wave exchange states by lane shuffles; the others
-    // go through LDS. (Every lane merges; only the lower slot of each pair goes on.)
+    // Levels whose two slots share a wave exchange states between lanes t * CG apart
+    // (16 or 32: row and half swaps, no LDS); the others go through LDS. (Every lane
+    // merges; only the lower slot of each pair goes on.)
     constexpr int kSlotsPerWave = kWave / CG < S ? kWave / CG : S;
 #pragma unroll
     for (int t = 1; t < kSlotsPerWave; t <<= 1) {
         MState other;
-        other.o.x = __shfl_xor(st.o.x, t * CG, kWave);
-        other.o.y = __shfl_xor(st.o.y, t * CG, kWave);
-        other.o.z = __shfl_xor(st.o.z, t * CG, kWave);
-        other.o.w = __shfl_xor(st.o.w, t * CG, kWave);
-        other.l = __shfl_xor(st.l, t * CG, kWave);
-        other.m = __shfl_xor(st.m, t * CG, kWave);
+        other.o.x = xor_lanes(st.o.x, t * CG);
+        other.o.y = xor_lanes(st.o.y, t * CG);
+        other.o.z = xor_lanes(st.o.z, t * CG);
+        other.o.w = xor_lanes(st.o.w, t * CG);
+        other.l = xor_lanes(st.l, t * CG);
+        other.m = xor_lanes(st.m, t * CG);
         st = merge_states(st, other);
     }
 #pragma unroll
