@@ -105,6 +105,44 @@ def test_partial_states_match_oracle_windows():
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+# tokens in one wave-wide block: 4 tokens per lane x the rows a wave-wide load covers
+# (64 lanes / the 16-byte segments of a row)
+BLOCK_TOKENS = {("bf16", 128): 16, ("bf16", 64): 32, ("f32", 128): 8, ("f32", 64): 16}
+
+
+@pytest.mark.parametrize("grid", ["one per CU", "small"])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+def test_partial_states_across_block_loop_phases(dtype, d, grid):
+    # Each wave streams its blocks in turns of the register ring: turns whose prefetches
+    # all lie inside the chunk issue them unconditionally, the last few turns under a
+    # branch, and one wave then takes the chunk's partial block. Chunks of 0 to 25 full
+    # blocks, with and without a partial block, put every wave in every phase, with
+    # 4 waves per workgroup (a grid of one workgroup per CU) and with 8 (a small grid).
+    # Every state is checked against the oracle over its own window.
+    bt = BLOCK_TOKENS[(dtype, d)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B, Hq, Hkv = (cus // 64, 32, 8) if grid == "one per CU" else (1, 8, 2)
+    if grid == "one per CU" and cus % 64:
+        pytest.skip(f"{cus} CUs is no multiple of 64")
+    for nfull in (0, 1, 3, 8, 9, 11, 12, 16, 17, 25):
+        for tail in (0, 3):
+            chunk = nfull * bt + tail
+            if chunk == 0:
+                continue
+            N = 8 * chunk  # 8 chunks per row: 8 x 8 head groups x B workgroups
+            lens = [N, N - chunk // 2 - 1, 3 * chunk + 1, N][:B] if B > 1 else [N - 1]
+            lens += [N] * (B - len(lens))
+            inp = W.random_decode(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype=dtype, seed=nfull * 10 + tail, seqlens=lens)
+            log(f"loop phases: {dtype} d={d} {grid} chunk={chunk} ({nfull} blocks + {tail}) B={B} lens={lens}")
+            q, k, v, sl = upload(inp)
+            po, pl = ta.partial(q, k, v, sl, chunk=chunk)
+            torch.cuda.synchronize()
+            po, pl = po.cpu().numpy(), pl.cpu().numpy()
+            for i in range(8):
+                ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens, t_begin=i * chunk, t_end=(i + 1) * chunk)
+                assert_close(po[:, :, i], pl[:, :, i], ro, rl, dtype, what=f"chunk {chunk} state {i}")
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,N,d,chunk,seqlens", [
     # 48 workgroups: write-back state stores
     (3, 8, 2, 2400, 128, 300, [2400, 700, 0]),
