@@ -123,6 +123,22 @@ __device__ __forceinline__ void seg_widen<float>(const uint4& s, float (&f)[4]) 
     f[2] = __uint_as_float(s.z); f[3] = __uint_as_float(s.w);
 }
 
+// One wave-wide load of 16-byte segments through a buffer resource whose base is the
+// load's first row (wave-uniform, in scalar registers) and whose range is the `span`
+// bytes the load covers; `off` is this lane's offset from that row. The address sum
+// happens in the load unit: a global load would need a 64-bit vector add per lane
+// first, because the compiler folds the lane offset into a per-lane pointer. A lane
+// offset past the span would read zeros instead of other memory. Nontemporal, like
+// load_stream. The fourth word of the resource, 0x00020000, is the gfx9 family's
+// setting for untyped 32-bit data.
+__device__ __forceinline__ uint4 load_rows(const char* row0, uint32_t span, uint32_t off) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(row0), (short)0, (int)span, 0x00020000);
+    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, TA_STREAM_NT ? 2 : 0);
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 __device__ __forceinline__ const uint4* row_ptr(const char* base, int64_t row, int64_t row_bytes) {
     return reinterpret_cast<const uint4*>(base + row * row_bytes);
 }
@@ -203,13 +219,19 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
 
     // Row addresses: a wave-uniform base (scalar registers) for each row of a block plus
     // this lane's 32-bit offset inside its row group (row stride x row-group index +
-    // 16-byte segment), so a full block costs no per-lane address arithmetic.
+    // 16-byte segment). Full blocks load through buffer resources built on that base
+    // (load_rows), so the address sum happens in the load unit and a full block costs
+    // no per-lane address arithmetic.
     const int64_t ks_bytes = p.k_st * (int64_t)sizeof(T);
     const int64_t vs_bytes = p.v_st * (int64_t)sizeof(T);
     const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.k_sb + (int64_t)g * p.k_sh) * (int64_t)sizeof(T);
     const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.v_sb + (int64_t)g * p.v_sh) * (int64_t)sizeof(T);
     const uint32_t koff = (uint32_t)(rg * ks_bytes) + (uint32_t)(seg * 16);
     const uint32_t voff = (uint32_t)(rg * vs_bytes) + (uint32_t)(seg * 16);
+    // bytes one wave-wide load spans from its first row: RG rows of the tensor's stride
+    // (below 2 GiB, as the token stride is below 256 MiB)
+    const uint32_t k_span = (uint32_t)((RG - 1) * ks_bytes) + (uint32_t)(D * sizeof(T));
+    const uint32_t v_span = (uint32_t)((RG - 1) * vs_bytes) + (uint32_t)(D * sizeof(T));
 
     // Running state of this lane's row group. The lane keeps the running max and sum
     // of head (lane & (GT - 1)) (every lane of the row holding that head keeps the same
@@ -227,8 +249,8 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
         for (int j = 0; j < TPL; ++j) {
             const char* kr = kbase + (t0 + j * RG) * ks_bytes;
             const char* vr = vbase + (t0 + j * RG) * vs_bytes;
-            kb[j] = load_stream(reinterpret_cast<const uint4*>(kr + koff));
-            vb[j] = load_stream(reinterpret_cast<const uint4*>(vr + voff));
+            kb[j] = load_rows(kr, k_span, koff);
+            vb[j] = load_rows(vr, v_span, voff);
         }
     };
     // The chunk's last, partial block: rows past its end are clamped to its last row
