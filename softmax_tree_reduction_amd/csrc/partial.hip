@@ -410,7 +410,7 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
     // only. A prefetch under a branch would merge that count with the branch's
     // not-taken side, and each block would then also wait for the prefetch just
     // issued, leaving the memory latency of every turn exposed. The last turns
-    // (at most 2 NBUF - 1 blocks per wave) take the branch.
+    // (at most 2 NBUF - 2 blocks per wave) take the branch.
     // The several-chunks kernel for bf16 with d = 128 runs the branch form
     // throughout: there the workgroup streams 8192 tokens or more alone on its CU,
     // and that form measured 0.7-1.5% faster (1M and 4 x 512k tokens), while the
