@@ -409,8 +409,10 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
     // count of loads in flight stays exact and block blk waits for its own loads
     // only. A prefetch under a branch would merge that count with the branch's
     // not-taken side, and each block would then also wait for the prefetch just
-    // issued, leaving the memory latency of every turn exposed. The last turns
-    // (at most 2 NBUF - 2 blocks per wave) take the branch.
+    // issued, leaving the memory latency of every turn exposed. The at most
+    // 2 NBUF - 2 blocks per wave left after the steady turns run as straight-line
+    // code per case (with NBUF = 2: one or two blocks), or through the branch form
+    // for other ring depths.
     // The several-chunks kernel for bf16 with d = 128 runs the branch form
     // throughout: there the workgroup streams 8192 tokens or more alone on its CU,
     // and that form measured 0.7-1.5% faster (1M and 4 x 512k tokens), while the
@@ -446,6 +448,21 @@ __device__ __forceinline__ void chunk_state(const PartialParams& p, int b, int h
                 blk += NW;
                 after_block();
             }
+        }
+        if constexpr (kSteady && NBUF == 2) {
+            // The ring holds block blk; one or two blocks are left. Each path issues
+            // its loads unconditionally, so the waits stay exact here too.
+            if (blk + NW < nfull) {
+                load_full(c0 + (blk + NW) * BT, kb[1], vb[1]);
+                compute_block(std::false_type{}, c0 + blk * BT, kb[0], vb[0]);
+                after_block();
+                compute_block(std::false_type{}, c0 + (blk + NW) * BT, kb[1], vb[1]);
+                after_block();
+            } else if (blk < nfull) {
+                compute_block(std::false_type{}, c0 + blk * BT, kb[0], vb[0]);
+                after_block();
+            }
+            blk = nfull;  // every full block of this wave is done
         }
         bool more = blk < nfull;
         while (more) {

@@ -114,8 +114,9 @@ BLOCK_TOKENS = {("bf16", 128): 16, ("bf16", 64): 32, ("f32", 128): 8, ("f32", 64
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
 def test_partial_states_across_block_loop_phases(dtype, d, grid):
     # Each wave streams its blocks in turns of the register ring: turns whose prefetches
-    # all lie inside the chunk issue them unconditionally, the last few turns under a
-    # branch, and one wave then takes the chunk's partial block. Chunks of 0 to 25 full
+    # all lie inside the chunk issue them unconditionally, the one or two blocks left
+    # after them run as straight-line code per case, and one wave then takes the
+    # chunk's partial block. Chunks of 0 to 25 full
     # blocks, with and without a partial block, put every wave in every phase, with
     # 4 waves per workgroup (a grid of one workgroup per CU) and with 8 (a small grid).
     # Every state is checked against the oracle over its own window.
