@@ -176,8 +176,9 @@ int ta_partial(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v,
 
 /*
  * ta_stream_read - measurement utility, not part of the decode path: reads
- * `bytes` bytes of device memory at `buf` once, with the 16-byte nontemporal
- * loads the partial kernel streams K and V with, and computes nothing from them.
+ * `bytes` bytes of device memory at `buf` once, with 16-byte nontemporal loads
+ * (the width and cache policy of the partial kernel's K and V loads), and
+ * computes nothing from them.
  * Timing it gives the device's practical read ceiling for this access.
  *
  *   buf     device pointer, 16-byte aligned; bytes >= 0, a multiple of 16

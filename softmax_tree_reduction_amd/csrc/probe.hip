@@ -1,6 +1,7 @@
-// Read-bandwidth probe: streams a buffer once with the 16-byte nontemporal loads
-// the partial kernel reads K and V with, and computes nothing from the data. Its
-// rate is the device's practical read ceiling for that kind of access.
+// Read-bandwidth probe: streams a buffer once with 16-byte nontemporal loads (the
+// width and cache policy of the partial kernel's K and V loads, which go through
+// buffer resources; these are plain global loads) and computes nothing from the
+// data. Its rate is the device's practical read ceiling for that kind of access.
 #include "device_common.h"
 #include "kernels.h"
 
