@@ -71,6 +71,35 @@ def test_token_major_strided_cache():
     check_small(inp, 300, layout="bnhd", what="token-major cache")
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 128)])
+def test_token_stride_at_the_limit(dtype, d):
+    # Rows 256 MiB - 256 B apart, just under the largest token stride the library takes:
+    # one wave-wide load then spans up to 7 such strides (bf16 d = 64), the largest
+    # offsets the partial kernel forms. Two full blocks and a partial one, in one chunk
+    # and in chunks of one block; the bytes between rows are never written.
+    bt = BLOCK_TOKENS[(dtype, d)]
+    N = 2 * bt + 3
+    inp = W.random_decode(B=1, Hq=4, Hkv=1, N=N, d=d, dtype=dtype, seed=d + N, seqlens=[N])
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    es = 2 if dtype == "bf16" else 4
+    stride = ((1 << 28) - 256) // es  # elements
+    q, kc, vc, _ = upload(inp)
+    log(f"token stride limit: {dtype} d={d} N={N} stride={stride * es} B, {N * stride * es / 2**30:.1f} GiB per tensor")
+    k_big = torch.empty(N * stride, dtype=tdt, device="cuda")
+    v_big = torch.empty(N * stride, dtype=tdt, device="cuda")
+    k_big.view(N, stride)[:, :d] = kc[0, 0]
+    v_big.view(N, stride)[:, :d] = vc[0, 0]
+    k = k_big.as_strided((1, 1, N, d), (N * stride, N * stride, stride, 1))
+    v = v_big.as_strided((1, 1, N, d), (N * stride, N * stride, stride, 1))
+    ref_o, ref_l = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+    for chunk in (N, bt):
+        out, lse = ta.decode(q, k, v, None, chunk=chunk)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, dtype, what=f"stride limit chunk {chunk}")
+    del k, v, k_big, v_big
+    torch.cuda.empty_cache()
+
+
 def test_peaked_keys_small():
     wl = W.DecodeWorkload("peaked-small", B=2, Hq=32, Hkv=8, d=128, N=8192, chunk=1024, dtype="bf16",
                           spike_frac=0.01, spike_scale=8.0)
