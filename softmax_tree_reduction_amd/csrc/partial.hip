@@ -579,7 +579,9 @@ int device_cus() {
 // get more waves per workgroup (measured 16-20% faster at 64 and 128 workgroups,
 // even at 256, slower from 512 on).
 // Workgroups of the per-chunk kernel one CU holds at once (limited by its registers
-// and LDS), from the runtime; 0 if it cannot say.
+// and LDS), from the runtime; 0 if it cannot say. One value serves every device: the
+// library holds gfx950 code only, and the count depends on the kernel and the
+// architecture.
 template <typename T, int D, int GT, int NW, int TPL, int NBUF>
 int per_chunk_capacity() {
     static std::atomic<int> cache{0};
