@@ -134,6 +134,28 @@ def test_partial_states_match_oracle_windows():
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+@pytest.mark.parametrize("P", [8, 32, 33, 64])
+def test_ragged_chunk_orders_match_oracle_windows(P):
+    # Ragged grids with 8 head groups per sequence and at most 32 chunks per row are
+    # walked chunk-major, the others with the chunk index fastest (rotated per row
+    # when the row has a multiple of 8 chunks): every state must land in its own slot
+    chunk = 64
+    N = P * chunk
+    lens = [N, min(700, N - 3), N - 1, 0, 65]
+    inp = W.random_decode(B=5, Hq=32, Hkv=8, N=N, d=128, dtype="bf16", seed=P, seqlens=lens)
+    log(f"chunk orders: P={P} N={N} lens={lens}")
+    q, k, v, sl = upload(inp)
+    po, pl = ta.partial(q, k, v, sl, chunk=chunk)
+    out, lse = ta.decode(q, k, v, sl, chunk=chunk)
+    torch.cuda.synchronize()
+    po, pl = po.cpu().numpy(), pl.cpu().numpy()
+    for i in range(P):
+        ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens, t_begin=i * chunk, t_end=(i + 1) * chunk)
+        assert_close(po[:, :, i], pl[:, :, i], ro, rl, "bf16", what=f"P={P} state {i}")
+    ref_o, ref_l = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "bf16", what=f"P={P} decode")
+
+
 # tokens in one wave-wide block: 4 tokens per lane x the rows a wave-wide load covers
 # (64 lanes / the 16-byte segments of a row)
 BLOCK_TOKENS = {("bf16", 128): 16, ("bf16", 64): 32, ("f32", 128): 8, ("f32", 64): 16}
