@@ -62,6 +62,25 @@ def measured_traffic(wl_name: str):
     return t.get("bytes_per_launch")
 
 
+def host_cpu() -> dict:
+    """The host's CPU model (from /proc/cpuinfo, as lscpu reports it) and the logical
+    CPUs the machine has and this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
 def cpu_baseline(inp, wl, budget_s: float):
     """The oracle, untouched, on the full step (all rows), repeated within a time budget."""
     import oracle
@@ -88,7 +107,7 @@ def cpu_baseline(inp, wl, budget_s: float):
         one = time.perf_counter() - t0
     finally:
         oracle.set_num_threads(cores)
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle", "cpu": host_cpu(),
             "sample": f"the full step of {wl.name} (all {wl.B * wl.Hq} query rows, {int(sum(inp.seqlens))} tokens "
                       f"per KV head), float64 two-pass definition, median of {len(times)} runs, "
                       f"{med * 1e3:.1f} ms per step",
@@ -199,6 +218,110 @@ def bench_combine(args, dev) -> int:
     return 0
 
 
+def bench_floor(args, dev) -> int:
+    """Floors of the merge stage. Prints one JSON line with, in µs per call:
+    - empty_launch: ta_stream_read over 16 bytes (one workgroup, one load), replayed
+      from a captured graph: what a launch costs with no work;
+    - read_combine_bytes: ta_stream_read over the merge workload's 34.3 MB, rotated
+      over resident copies as --mode combine rotates its inputs (graph replay);
+    - combine: ta_combine on the merge workload (32 x 32 rows of 64 states), same way;
+    - on the 128k decode workload, eager loops over the cache rotation: ta_partial
+      alone, ta_partial followed by the empty launch, ta_partial followed by ta_combine
+      of its states, and ta_decode. The differences to ta_partial alone are what a
+      dependent second launch, and the merge, add to a decode step."""
+    import numpy as np
+    import torch
+
+    import softmax_tree_reduction_amd as ta
+    import workloads as W
+
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def graph_us(fn, reps):
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fn(0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(reps):
+                fn(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        del graph
+        return ev0.elapsed_time(ev1) / reps * 1e3
+
+    def eager_us(fn, reps):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(reps):
+            fn(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps * 1e3
+
+    settled_ms, _, ceiling = settle_and_read_ceiling(ta, torch, dev, stream, args.settle_ms)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    tiny = torch.zeros(16, dtype=torch.uint8, device=dev)
+    res = {"mode": "floor", "settle_ms": round(settled_ms, 1), "read_ceiling_GB_per_s": round(ceiling, 1)}
+    res["empty_launch_us"] = round(graph_us(lambda i: ta.stream_read(tiny, sink), args.steps), 2)
+
+    cw = W.COMBINE_WORKLOADS["combine_64x128"]
+    ci = W.make_combine_inputs(cw, args.seed)
+    nbytes = (ci.partial_o.nbytes + ci.partial_lse.nbytes) + cw.B * cw.H * (cw.d + 1) * 4
+    copies = max(1, math.ceil(args.min_rotation_bytes / nbytes))
+    pos = [torch.from_numpy(ci.partial_o).to(dev) for _ in range(copies)]
+    pls = [torch.from_numpy(ci.partial_lse).to(dev) for _ in range(copies)]
+    flat = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    out = torch.empty(cw.B, cw.H, cw.d, dtype=torch.float32, device=dev)
+    lse = torch.empty(cw.B, cw.H, dtype=torch.float32, device=dev)
+    res["combine_bytes"] = nbytes
+    res["read_combine_bytes_us"] = round(graph_us(lambda i: ta.stream_read(flat[i % copies], sink), args.steps), 2)
+    res["combine_us"] = round(graph_us(lambda i: ta.combine(pos[i % copies], pls[i % copies], out=out, lse=lse),
+                                       args.steps), 2)
+    del pos, pls, flat
+
+    wl = W.WORKLOADS["gqa8b_128k"]
+    inp = W.make_decode_inputs(wl, args.seed)
+    to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k0, v0 = to(inp.q), to(inp.k), to(inp.v)
+    ncopies = max(1, math.ceil(args.min_rotation_bytes / (2 * k0.numel() * 2)))
+    ks, vs = [k0] + [k0.clone() for _ in range(ncopies - 1)], [v0] + [v0.clone() for _ in range(ncopies - 1)]
+    P = -(-wl.N // wl.chunk)
+    po = torch.empty(wl.B, wl.Hq, P, wl.d, dtype=torch.float32, device=dev)
+    pl = torch.empty(wl.B, wl.Hq, P, dtype=torch.float32, device=dev)
+    o1 = torch.empty(wl.B, wl.Hq, wl.d, dtype=torch.float32, device=dev)
+    l1 = torch.empty(wl.B, wl.Hq, dtype=torch.float32, device=dev)
+    part = lambda i: ta.partial(q, ks[i % ncopies], vs[i % ncopies], None, chunk=wl.chunk, partial_o=po, partial_lse=pl)
+
+    def part_empty(i):
+        part(i)
+        ta.stream_read(tiny, sink)
+
+    def part_combine(i):
+        part(i)
+        ta.combine(po, pl, out=o1, lse=l1)
+
+    dec = lambda i: ta.decode(q, ks[i % ncopies], vs[i % ncopies], None, chunk=wl.chunk, out=o1, lse=l1)
+    step = {"workload": wl.name}
+    for name, f in (("partial_us", part), ("partial_then_empty_launch_us", part_empty),
+                    ("partial_then_combine_us", part_combine), ("decode_us", dec)):
+        step[name] = round(eager_us(f, args.steps), 2)
+    step["combine_alone_us"] = round(graph_us(lambda i: ta.combine(po, pl, out=o1, lse=l1), args.steps), 2)
+    res["step_128k"] = step
+    print(json.dumps(res))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,10 +337,11 @@ def main() -> int:
     ap.add_argument("--suggested-chunk", action="store_true",
                     help="also time the step at the chunk ta_suggest_chunk returns (reported as suggested_chunk)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
-    ap.add_argument("--mode", choices=["step", "partial", "copy", "combine"], default="step",
+    ap.add_argument("--mode", choices=["step", "partial", "copy", "combine", "floor"], default="step",
                     help="step: the benchmark line (default); partial: only the timed partial-kernel launches "
                          "(for counter runs); copy: a plain device copy of --copy-mib MiB (counter calibration); "
-                         "combine: the standalone ta_combine workload (64 fp32 states per head, 32 x 32 heads)")
+                         "combine: the standalone ta_combine workload (64 fp32 states per head, 32 x 32 heads); "
+                         "floor: launch and streaming floors of the merge stage")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--n-parts", type=int, default=0,
                     help="combine mode: states per row (default: the workload's 64)")
@@ -257,6 +381,8 @@ def main() -> int:
         return 0
     if args.mode == "combine":
         return bench_combine(args, dev)
+    if args.mode == "floor":
+        return bench_floor(args, dev)
     print(f"bench: generating {wl.name} (seed {args.seed})", file=sys.stderr, flush=True)
     inp = W.make_decode_inputs(wl, args.seed)
     step_bytes = algorithmic_bytes(wl, inp.seqlens)
@@ -325,6 +451,18 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # the spread of the timed loop itself: the same K-step loop, timed the same way,
+    # run 5 more times (the per-step mean of each run)
+    loop_means = [ms_step]
+    for _ in range(5):
+        ev0.record(stream)
+        for i in range(args.steps):
+            ta.decode(q, ks[i % copies], vs[i % copies], sl, chunk=chunk, out=out, lse=lse)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        loop_means.append(ev0.elapsed_time(ev1) / args.steps)
+    loop_means.sort()
 
     # the spread of single steps, from a separate pass with an event after every step
     # (each event costs a few µs of its own, so these run longer than `value`'s loop)
@@ -423,8 +561,13 @@ def main() -> int:
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(ms_step * 1e3, 2),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "us_per_step_loops": {"median": round(loop_means[len(loop_means) // 2] * 1e3, 2),
+                              "min": round(loop_means[0] * 1e3, 2), "max": round(loop_means[-1] * 1e3, 2),
+                              "loops": len(loop_means),
+                              "note": "per-step mean of the timed K-step loop and of 5 more runs of it, timed alike"},
         "us_per_step_dist": {"median": round(pct(0.5), 2), "p10": round(pct(0.1), 2), "p90": round(pct(0.9), 2),
-                             "note": "separate pass, an event after every step (adds the events' own cost)"},
+                             "note": "single steps from a separate pass with an event recorded after every step; "
+                                     "each event adds its own few µs, so these run longer than the timed loop"},
         "us_per_step_warm": round(ms_warm * 1e3, 2),
         "suggested_chunk": alt,
         "read_ceiling": {"value": round(ceiling, 1), "unit": "GB/s", "kernel": "ta_stream_read",

@@ -20,7 +20,8 @@
  *
  * Conventions shared by every entry point:
  *  - Tensors are passed as host-side ta_tensor descriptors whose `data`
- *    points to device memory on the current HIP device. The descriptors are
+ *    points to device memory on the current HIP device (it may be NULL for a
+ *    tensor with no elements, which is never accessed). The descriptors are
  *    read during the call only; the library keeps no pointer after it returns.
  *    The caller owns every tensor.
  *  - Strides are in elements, never negative. In q, k, v, out and partial_o the
@@ -96,13 +97,16 @@ enum {
  * a token stride of k and v below 256 MiB; P = ceil(N / chunk) <= 65535 * 128
  * (d = 128) or 65535 * 256 (d = 64), the states one merge pass takes
  * (TA_ERR_UNSUPPORTED beyond any of these).
- * Needs Hq * P * (d + 1) * 4 bytes of device workspace per sequence
+ * Needs about Hq * P * (d + 1) * 4 bytes of device workspace per sequence
  * (P = ceil(N / chunk)). The library keeps one workspace buffer per (device,
  * stream), allocated with hipMallocAsync on that stream the first time it is
  * needed and grown when a call needs more; it is held until the process ends.
- * Calls on one stream run in stream order and so never share it concurrently.
- * While the stream is being captured into a graph the workspace is allocated
- * and released inside the captured work instead.
+ * Host threads may call concurrently, on the same stream or on different
+ * ones: a call holds its stream's buffer from its first launch until it
+ * returns, so the kernels of concurrent calls on one stream are enqueued back
+ * to back (in an unspecified order) and never read each other's partial
+ * states. While the stream is being captured into a graph the workspace is
+ * allocated and released inside the captured work instead.
  */
 int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v,
               const int32_t* seqlens, const ta_tensor* out, const ta_tensor* lse,
@@ -167,8 +171,10 @@ int ta_combine_chain(const ta_tensor* partial_o, const ta_tensor* partial_lse, i
  *   partial_lse  [B, Hq, P]    f32
  * Chunk i of sequence b covers tokens [i*chunk, min((i+1)*chunk, n_b)); a
  * chunk with no tokens gets o_i = 0 and lse_i = -inf. Entries i >= ceil(N/chunk)
- * are not written. ta_combine over these P states equals ta_decode.
- * Allocates nothing.
+ * are not written, except that an empty cache (N = 0) writes the empty state
+ * to entry 0 of every row when P >= 1 (the one state ta_decode merges then).
+ * ta_combine over these states (ceil(N/chunk) of them, or 1 when N = 0)
+ * equals ta_decode bit for bit. Allocates nothing.
  */
 int ta_partial(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v,
                const int32_t* seqlens, const ta_tensor* partial_o, const ta_tensor* partial_lse,

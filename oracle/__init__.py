@@ -34,14 +34,28 @@ _lib = None
 F32, BF16 = 0, 1
 
 
+# ORACLE_SANITIZE=1 builds and loads a copy instrumented with AddressSanitizer and
+# UndefinedBehaviorSanitizer (any finding aborts the process). The process must
+# then start with gcc's libasan preloaded (LD_PRELOAD), as a non-instrumented
+# Python interpreter loads the library.
+_SAN_LIB = os.path.join(_HERE, "liboracle_asan.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def _sanitized() -> bool:
+    return os.environ.get("ORACLE_SANITIZE", "") == "1"
+
+
 def build(force: bool = False) -> str:
     """Compile oracle.c with gcc (float64, OpenMP). Returns the library path."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + f".tmp{os.getpid()}"
+    lib = _SAN_LIB if _sanitized() else _LIB
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + f".tmp{os.getpid()}"
         subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-                        "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"], check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+                        "-Wall", "-Wextra", *(_SAN_FLAGS if _sanitized() else []), _SRC, "-o", tmp, "-lm"],
+                       check=True)
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():

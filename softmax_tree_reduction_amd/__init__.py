@@ -25,11 +25,13 @@ __all__ = ["decode", "partial", "combine", "PreparedDecode", "stream_read", "sug
 TA_OK, TA_ERR_NULL, TA_ERR_SHAPE, TA_ERR_DTYPE, TA_ERR_STRIDE, TA_ERR_ARG, TA_ERR_UNSUPPORTED, TA_ERR_HIP = \
     0, -1, -2, -3, -4, -5, -6, -7
 TA_F32, TA_BF16 = 0, 1
-EXPORTS = ("ta_decode", "ta_combine", "ta_combine_k", "ta_combine_chain", "ta_partial", "ta_stream_read",
-           "ta_suggest_chunk", "ta_last_error", "ta_version")
+EXPORTS = ("ta_decode", "ta_combine", "ta_combine_k", "ta_combine_chain", "ta_partial",
+           "ta_stream_read", "ta_suggest_chunk", "ta_last_error", "ta_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libtreeattn.so")
+# TA_LIBRARY names another build of the library to load (for instance the copy whose
+# host code runs under sanitizers); by default the in-tree libtreeattn.so.
+_LIB_PATH = os.environ.get("TA_LIBRARY") or os.path.join(_HERE, "libtreeattn.so")
 _lock = threading.Lock()
 _lib = None
 

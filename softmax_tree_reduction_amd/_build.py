@@ -28,8 +28,32 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
+# A copy of the library whose host code (argument validation, dispatch, workspace)
+# is instrumented with AddressSanitizer and UndefinedBehaviorSanitizer; the GPU code
+# is built as usual. A process using it needs clang's ASan runtime preloaded.
+SAN_LIB = os.path.join(HERE, "_build_san", "libtreeattn_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=all",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libsan"]
+
+
+def asan_runtime() -> str:
+    """Path of the ASan runtime of hipcc's clang (to preload into a process that
+    loads the sanitized library)."""
+    res = subprocess.run([hipcc(), "--print-file-name=libclang_rt.asan-x86_64.so"], check=True,
+                         capture_output=True, text=True).stdout.strip()
+    if not os.path.isabs(res) or not os.path.exists(res):
+        raise RuntimeError(f"clang ASan runtime not found ({res!r})")
+    return res
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Build SAN_LIB: host code under ASan and UBSan (any finding aborts)."""
+    return build(verbose, extra_flags=SAN_FLAGS, out=SAN_LIB, objdir=os.path.join(HERE, "_build_san"),
+                 link_flags=SAN_FLAGS)
+
+
 def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str = LIB,
-          objdir: str | None = None) -> str:
+          objdir: str | None = None, link_flags: list[str] | None = None) -> str:
     """Compile every source, link the shared library (in place by default), return its path."""
     cc = hipcc()
     objdir = objdir or os.path.join(HERE, "_build")
@@ -47,7 +71,7 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = out + f".tmp{os.getpid()}"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(link_flags or []), *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

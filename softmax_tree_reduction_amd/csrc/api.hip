@@ -40,13 +40,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // row 16-byte aligned; the lse tensors take any strides.
 int check_tensor(const ta_tensor* t, const char* name, int ndim, bool rows_of_d) {
     if (!t) return fail(TA_ERR_NULL, "%s: descriptor is NULL", name);
-    if (!t->data) return fail(TA_ERR_NULL, "%s: data pointer is NULL", name);
     if (t->ndim != ndim) return fail(TA_ERR_SHAPE, "%s: expected %d dimensions, got %d", name, ndim, t->ndim);
     if (t->dtype != TA_F32 && t->dtype != TA_BF16) return fail(TA_ERR_DTYPE, "%s: unknown dtype %d", name, t->dtype);
+    bool empty = false;
     for (int i = 0; i < ndim; ++i) {
         if (t->shape[i] < 0) return fail(TA_ERR_SHAPE, "%s: negative size in dimension %d", name, i);
         if (t->stride[i] < 0) return fail(TA_ERR_STRIDE, "%s: negative stride in dimension %d", name, i);
+        empty = empty || t->shape[i] == 0;
     }
+    // a tensor with no elements is never read or written, so its pointer may be NULL
+    if (!t->data && !empty) return fail(TA_ERR_NULL, "%s: data pointer is NULL", name);
     if (!rows_of_d) return TA_OK;
     if (t->shape[ndim - 1] > 1 && t->stride[ndim - 1] != 1)
         return fail(TA_ERR_STRIDE, "%s: the last dimension must be contiguous (stride 1), got %lld", name,
@@ -66,15 +69,19 @@ int hip_fail(hipError_t e, const char* what) {
 
 // Device scratch of one call, ordered on the call's stream. Outside graph capture
 // it is a buffer kept per (device, stream) and grown when a call needs more, so a
-// steady decode loop allocates nothing; work on one stream runs in order, so calls
-// on the same stream never overlap in it. Under graph capture the scratch is
-// allocated and released inside the captured work instead.
+// steady decode loop allocates nothing. The buffer's lock is held from acquire()
+// until the call returns, that is until its last kernel is enqueued: two host
+// threads calling on one stream then enqueue their kernels back to back, never
+// interleaved, so no call's merge reads another call's partial states, and a buffer
+// released when it grows is released behind every kernel already enqueued on it.
+// Under graph capture the scratch is allocated and released inside the captured
+// work instead.
 class CallWorkspace {
   public:
     explicit CallWorkspace(hipStream_t st) : st_(st) {}
     ~CallWorkspace() {
         if (owned_ && ptr_) (void)hipFreeAsync(ptr_, st_);
-    }
+    }  // lock_ is released after this body, once every launch of the call is enqueued
     CallWorkspace(const CallWorkspace&) = delete;
     CallWorkspace& operator=(const CallWorkspace&) = delete;
 
@@ -90,23 +97,28 @@ class CallWorkspace {
             owned_ = true;
             return TA_OK;
         }
-        std::lock_guard<std::mutex> lock(cache_mu());
-        Entry& w = cache()[{dev, reinterpret_cast<uintptr_t>(st_)}];
-        if (w.bytes < bytes) {
-            const size_t nb = bytes > w.bytes + w.bytes / 2 ? bytes : w.bytes + w.bytes / 2;
+        Entry* w = nullptr;
+        {
+            std::lock_guard<std::mutex> g(cache_mu());
+            w = &cache()[{dev, reinterpret_cast<uintptr_t>(st_)}];  // map nodes never move or go away
+        }
+        lock_ = std::unique_lock<std::mutex>(w->mu);
+        if (w->bytes < bytes) {
+            const size_t nb = bytes > w->bytes + w->bytes / 2 ? bytes : w->bytes + w->bytes / 2;
             void* p = nullptr;
             if ((e = hipMallocAsync(&p, nb, st_)) != hipSuccess) return hip_fail(e, "hipMallocAsync (workspace)");
-            if (w.ptr) (void)hipFreeAsync(w.ptr, st_);
-            w.ptr = p;
-            w.bytes = nb;
+            if (w->ptr) (void)hipFreeAsync(w->ptr, st_);
+            w->ptr = p;
+            w->bytes = nb;
         }
-        ptr_ = w.ptr;
+        ptr_ = w->ptr;
         return TA_OK;
     }
     void* get() const { return ptr_; }
 
   private:
     struct Entry {
+        std::mutex mu;  // held by the call using the buffer, from acquire() until it returns
         void* ptr = nullptr;
         size_t bytes = 0;
     };
@@ -121,7 +133,12 @@ class CallWorkspace {
     hipStream_t st_;
     void* ptr_ = nullptr;
     bool owned_ = false;
+    std::unique_lock<std::mutex> lock_;
 };
+
+// Byte counts of scratch sub-buffers are rounded up to 256 bytes, so that every
+// sub-buffer starts 256-byte aligned (the merge reads and writes float4 rows).
+constexpr size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Leaves one merge workgroup takes: the binary kernel's tile (arity 0), or the
 // largest power of `arity` the arity-K kernel holds.
@@ -140,13 +157,19 @@ int check_merge_groups(int64_t n_parts, int64_t d, int arity) {
     return TA_OK;
 }
 
+// Bytes of one buffer of intermediate states: o [B, H, groups, d], then lse
+// [B, H, groups] from the next 256-byte boundary.
+size_t state_buffer_bytes(int64_t B, int64_t H, int64_t groups, int64_t d) {
+    return align256((size_t)(B * H * groups * d) * sizeof(float)) + align256((size_t)(B * H * groups) * sizeof(float));
+}
+
 // Bytes of intermediate states the merge needs when a row has more leaves than one
 // workgroup takes: two buffers of the first pass's output size.
 size_t combine_scratch_bytes(int64_t n_parts, int64_t B, int64_t H, int64_t d, int arity = 0) {
     const int64_t span = merge_span(d, arity);
     if (n_parts <= span) return 0;
     const int64_t groups = (n_parts + span - 1) / span;
-    return 2 * (size_t)(B * H * groups * (d + 1)) * sizeof(float);
+    return 2 * state_buffer_bytes(B, H, groups, d);
 }
 
 struct DecodeShape {
@@ -281,14 +304,14 @@ int run_combine(const float* po, const int64_t po_st[3], const float* pl, const 
     const int32_t* sl = seqlens;
     const int64_t first_groups = (n_parts + span - 1) / span;
     float* bufs[2] = {static_cast<float*>(scratch), nullptr};
-    if (scratch) bufs[1] = bufs[0] + B * H * first_groups * (d + 1);
+    if (scratch) bufs[1] = reinterpret_cast<float*>(static_cast<char*>(scratch) + state_buffer_bytes(B, H, first_groups, d));
     int which = 0;
     hipError_t e = hipSuccess;
 
     while (leaves > span) {
         const int64_t groups = (leaves + span - 1) / span;
         float* nxt_o = bufs[which];
-        float* nxt_l = nxt_o + B * H * groups * d;
+        float* nxt_l = reinterpret_cast<float*>(reinterpret_cast<char*>(nxt_o) + align256((size_t)(B * H * groups * d) * sizeof(float)));
         ta::CombineParams c{};
         c.po = cur_o;
         c.plse = cur_l;
@@ -330,6 +353,55 @@ int run_combine(const float* po, const int64_t po_st[3], const float* pl, const 
     return TA_OK;
 }
 
+// Workspace layout of one decode call: partial o [B, Hq, P, d], partial lse
+// [B, Hq, P] from the next 256-byte boundary, then the merge's intermediate states.
+struct DecodePlan {
+    int64_t P;            // partial states per row (an N = 0 cache has one empty state)
+    size_t lse_offset;    // bytes from the workspace start to partial lse
+    size_t merge_offset;  // bytes to the merge scratch
+    size_t merge_bytes;
+    size_t total_bytes;
+};
+
+int check_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const ta_tensor* out, const ta_tensor* lse,
+                 int32_t chunk, DecodeShape* s, DecodePlan* plan) {
+    int rc;
+    if ((rc = check_decode_inputs(q, k, v, chunk, s)) != TA_OK) return rc;
+    if ((rc = check_outputs(out, lse, s->B, s->Hq, s->d)) != TA_OK) return rc;
+    plan->P = s->N > 0 ? (s->N + chunk - 1) / chunk : 1;
+    if ((rc = check_merge_groups(plan->P, s->d, 0)) != TA_OK) return rc;
+    plan->lse_offset = align256((size_t)(s->B * s->Hq * plan->P * s->d) * sizeof(float));
+    plan->merge_offset = state_buffer_bytes(s->B, s->Hq, plan->P, s->d);
+    plan->merge_bytes = combine_scratch_bytes(plan->P, s->B, s->Hq, s->d);
+    plan->total_bytes = s->B > 0 ? plan->merge_offset + plan->merge_bytes : 0;
+    return TA_OK;
+}
+
+// Enqueues the partial kernel and the merge of one decode step on `st`, with the
+// partial states and merge scratch in `ws` (plan.total_bytes of device memory).
+int launch_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const int32_t* seqlens,
+                  const ta_tensor* out, const ta_tensor* lse, int32_t chunk, const DecodeShape& s,
+                  const DecodePlan& plan, void* ws, hipStream_t st) {
+    const int64_t P = plan.P;
+    float* po = static_cast<float*>(ws);
+    float* pl = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.lse_offset);
+    void* merge_scratch = plan.merge_bytes ? static_cast<char*>(ws) + plan.merge_offset : nullptr;
+    const int64_t po_st[3] = {s.Hq * P * s.d, P * s.d, s.d};
+    const int64_t pl_st[3] = {s.Hq * P, P, 1};
+    const int gt = heads_per_wg(s.Hq / s.Hkv);
+    // With seqlens the merge reads only the chunks below ceil(n / chunk) of each row, so
+    // the chunks past a sequence's end need not be written; without, every chunk of the
+    // grid holds tokens except the one of an N = 0 cache, which the merge does read.
+    ta::PartialParams p = partial_params(q, k, v, seqlens, po, po_st, pl, pl_st, s, chunk,
+                                         /*empty_states=*/seqlens == nullptr);
+    hipError_t e = ta::launch_partial(p, s.dt, (int)s.d, gt, (int)s.B, (int)s.Hq, (int)P, st);
+    if (e != hipSuccess) return hip_fail(e, "partial kernel launch");
+    const int64_t out_st[2] = {out->stride[0], out->stride[1]};
+    const int64_t lse_st[2] = {lse ? lse->stride[0] : 0, lse ? lse->stride[1] : 0};
+    return run_combine(po, po_st, pl, pl_st, P, seqlens, chunk, s.N, s.B, s.Hq, s.d, static_cast<float*>(out->data),
+                       out_st, lse ? static_cast<float*>(lse->data) : nullptr, lse_st, merge_scratch, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -366,12 +438,16 @@ int ta_partial(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const
     if ((rc = check_decode_inputs(q, k, v, chunk, &s)) != TA_OK) return rc;
     const int64_t P = (s.N + chunk - 1) / chunk;
     if ((rc = check_partials(partial_o, partial_lse, s.B, s.Hq, s.d, P, "partial_o", "partial_lse")) != TA_OK) return rc;
-    if (s.B == 0 || P == 0) return ok();
+    // An empty cache (N = 0) gives every row one empty state in slot 0, the state
+    // ta_decode merges for it, when the caller's tensors have that slot.
+    const int64_t P_launch = P > 0 ? P : (partial_o->shape[2] > 0 ? 1 : 0);
+    if (s.B == 0 || P_launch == 0) return ok();
     const int gt = heads_per_wg(s.Hq / s.Hkv);
     ta::PartialParams p = partial_params(q, k, v, seqlens, static_cast<float*>(partial_o->data), partial_o->stride,
                                          static_cast<float*>(partial_lse->data), partial_lse->stride, s, chunk,
                                          /*empty_states=*/true);
-    hipError_t e = ta::launch_partial(p, s.dt, (int)s.d, gt, (int)s.B, (int)s.Hq, (int)P, static_cast<hipStream_t>(stream));
+    hipError_t e = ta::launch_partial(p, s.dt, (int)s.d, gt, (int)s.B, (int)s.Hq, (int)P_launch,
+                                      static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "partial kernel launch");
     return ok();
 }
@@ -379,35 +455,14 @@ int ta_partial(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const
 int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const int32_t* seqlens,
               const ta_tensor* out, const ta_tensor* lse, int32_t chunk, void* stream) {
     DecodeShape s;
+    DecodePlan plan;
     int rc;
-    if ((rc = check_decode_inputs(q, k, v, chunk, &s)) != TA_OK) return rc;
-    if ((rc = check_outputs(out, lse, s.B, s.Hq, s.d)) != TA_OK) return rc;
+    if ((rc = check_decode(q, k, v, out, lse, chunk, &s, &plan)) != TA_OK) return rc;
     if (s.B == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int64_t P = s.N > 0 ? (s.N + chunk - 1) / chunk : 1;  // N = 0: one empty state per row
-    const size_t part_bytes = (size_t)(s.B * s.Hq * P * (s.d + 1)) * sizeof(float);
-    if ((rc = check_merge_groups(P, s.d, 0)) != TA_OK) return rc;
-    const size_t merge_bytes = combine_scratch_bytes(P, s.B, s.Hq, s.d);
     CallWorkspace ws(st);
-    if ((rc = ws.acquire(part_bytes + merge_bytes)) != TA_OK) return rc;
-    float* po = static_cast<float*>(ws.get());
-    float* pl = po + s.B * s.Hq * P * s.d;
-    void* merge_scratch = merge_bytes ? static_cast<char*>(ws.get()) + part_bytes : nullptr;
-    const int64_t po_st[3] = {s.Hq * P * s.d, P * s.d, s.d};
-    const int64_t pl_st[3] = {s.Hq * P, P, 1};
-    const int gt = heads_per_wg(s.Hq / s.Hkv);
-    // With seqlens the merge reads only the chunks below ceil(n / chunk) of each row, so
-    // the chunks past a sequence's end need not be written; without, every chunk of the
-    // grid holds tokens except the one of an N = 0 cache, which the merge does read.
-    ta::PartialParams p = partial_params(q, k, v, seqlens, po, po_st, pl, pl_st, s, chunk,
-                                         /*empty_states=*/seqlens == nullptr);
-    hipError_t e = ta::launch_partial(p, s.dt, (int)s.d, gt, (int)s.B, (int)s.Hq, (int)P, st);
-    if (e != hipSuccess) return hip_fail(e, "partial kernel launch");
-    const int64_t out_st[2] = {out->stride[0], out->stride[1]};
-    const int64_t lse_st[2] = {lse ? lse->stride[0] : 0, lse ? lse->stride[1] : 0};
-    rc = run_combine(po, po_st, pl, pl_st, P, seqlens, chunk, s.N, s.B, s.Hq, s.d, static_cast<float*>(out->data),
-                     out_st, lse ? static_cast<float*>(lse->data) : nullptr, lse_st, merge_scratch, st);
-    if (rc != TA_OK) return rc;
+    if ((rc = ws.acquire(plan.total_bytes)) != TA_OK) return rc;
+    if ((rc = launch_decode(q, k, v, seqlens, out, lse, chunk, s, plan, ws.get(), st)) != TA_OK) return rc;
     return ok();
 }
 

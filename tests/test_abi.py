@@ -109,6 +109,20 @@ def test_decode_validation(mutate, code, needle):
     assert needle in msg
 
 
+def test_null_data_is_accepted_only_for_tensors_without_elements():
+    # an empty cache (N = 0) may come with NULL k and v pointers; validation passes
+    # them (on a machine without a GPU the call then fails on the device query)
+    a = good(N=0)
+    a["k"].data = None
+    a["v"].data = None
+    rc, msg = call_decode(a)
+    assert rc != ta.TA_ERR_NULL, msg
+    a = good(N=1)
+    a["k"].data = None
+    rc, msg = call_decode(a)
+    assert rc == ta.TA_ERR_NULL and "k" in msg
+
+
 def test_decode_unsupported_and_bad_chunk():
     rc, msg = call_decode(good(d=96))
     assert rc == ta.TA_ERR_UNSUPPORTED and "96" in msg
