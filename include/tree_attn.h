@@ -113,6 +113,28 @@ int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v,
               int32_t chunk, void* stream);
 
 /*
+ * ta_decode_noalloc - ta_decode for callers that cannot allocate device memory
+ * (code under graph capture, serving loops or harnesses that forbid hipMalloc).
+ *
+ * Arguments, semantics, supported sizes and results are those of ta_decode,
+ * bit for bit (the same kernels run). The partial states and the merge's
+ * scratch live in one static device array of 64 MiB (67108864 bytes) held by
+ * every device the library runs on, from the library's first use on it until
+ * the process ends, instead of in library workspace. The call allocates and
+ * frees nothing. A step needs about B * Hq * P * (d + 1) * 4 bytes of it
+ * (P = ceil(N / chunk)); a call needing more than 64 MiB returns
+ * TA_ERR_UNSUPPORTED before any launch. Nothing in the array needs clearing
+ * between calls: every state a call reads it has written first.
+ * Every call on one device uses the same array: two calls whose work can
+ * overlap on the device (on different streams with no ordering between them)
+ * race and give wrong results. Calls from several host threads on one stream
+ * are serialised by the library and do not race.
+ */
+int ta_decode_noalloc(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v,
+                      const int32_t* seqlens, const ta_tensor* out, const ta_tensor* lse,
+                      int32_t chunk, void* stream);
+
+/*
  * ta_combine - merge n_parts partial states per row by the binary tree, then
  * normalise ("Core Innovation 1" step 3 and "Core Innovation 2" of the page).
  *

@@ -17,7 +17,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["decode", "partial", "combine", "PreparedDecode", "stream_read", "suggest_chunk", "TreeAttnError",
+__all__ = ["decode", "decode_noalloc", "partial", "combine", "PreparedDecode", "stream_read", "suggest_chunk", "TreeAttnError",
            "library_path", "load_library",
            "TA_OK", "TA_ERR_NULL", "TA_ERR_SHAPE", "TA_ERR_DTYPE", "TA_ERR_STRIDE", "TA_ERR_ARG",
            "TA_ERR_UNSUPPORTED", "TA_ERR_HIP", "TaTensor", "EXPORTS"]
@@ -25,7 +25,7 @@ __all__ = ["decode", "partial", "combine", "PreparedDecode", "stream_read", "sug
 TA_OK, TA_ERR_NULL, TA_ERR_SHAPE, TA_ERR_DTYPE, TA_ERR_STRIDE, TA_ERR_ARG, TA_ERR_UNSUPPORTED, TA_ERR_HIP = \
     0, -1, -2, -3, -4, -5, -6, -7
 TA_F32, TA_BF16 = 0, 1
-EXPORTS = ("ta_decode", "ta_combine", "ta_combine_k", "ta_combine_chain", "ta_partial",
+EXPORTS = ("ta_decode", "ta_decode_noalloc", "ta_combine", "ta_combine_k", "ta_combine_chain", "ta_partial",
            "ta_stream_read", "ta_suggest_chunk", "ta_last_error", "ta_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +73,7 @@ def load_library():
             P = ctypes.POINTER(TaTensor)
             vp, i32 = ctypes.c_void_p, ctypes.c_int32
             lib.ta_decode.argtypes = [P, P, P, vp, P, P, i32, vp]
+            lib.ta_decode_noalloc.argtypes = [P, P, P, vp, P, P, i32, vp]
             lib.ta_partial.argtypes = [P, P, P, vp, P, P, i32, vp]
             lib.ta_combine.argtypes = [P, P, i32, P, P, vp]
             lib.ta_combine_k.argtypes = [P, P, i32, i32, P, P, vp]
@@ -81,7 +82,7 @@ def load_library():
             i64 = ctypes.c_int64
             lib.ta_suggest_chunk.argtypes = [i64, i64, i64, i64, i32]
             lib.ta_suggest_chunk.restype = ctypes.c_int32
-            for f in (lib.ta_decode, lib.ta_partial, lib.ta_combine, lib.ta_combine_k, lib.ta_combine_chain,
+            for f in (lib.ta_decode, lib.ta_decode_noalloc, lib.ta_partial, lib.ta_combine, lib.ta_combine_k, lib.ta_combine_chain,
                       lib.ta_stream_read):
                 f.restype = ctypes.c_int
             lib.ta_last_error.restype = ctypes.c_char_p
@@ -173,6 +174,26 @@ def decode(q, k, v, seqlens=None, chunk: int = 2048, out=None, lse=None, stream=
     dq, dk, dv, do, dl = _desc(q), _desc(k), _desc(v), _desc(out), _desc(lse)
     by = ctypes.byref
     _call(dev, stream, lambda s: lib.ta_decode(by(dq), by(dk), by(dv), sl, by(do), by(dl), int(chunk), s))
+    return out, lse
+
+
+def decode_noalloc(q, k, v, seqlens=None, chunk: int = 2048, out=None, lse=None, stream=None):
+    """ta_decode_noalloc: decode() whose partial states live in the library's static
+    device scratch (64 MiB per device) instead of allocated workspace. The library
+    allocates nothing; out and lse are allocated here only when not given. Calls
+    whose work overlaps on one device (different unordered streams) race."""
+    import torch
+    dev = _same_device(q, k, v, out, lse)
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    sl = _seqlens_ptr(seqlens, B, dev)
+    lib = _lib or load_library()
+    dq, dk, dv, do, dl = _desc(q), _desc(k), _desc(v), _desc(out), _desc(lse)
+    by = ctypes.byref
+    _call(dev, stream, lambda s: lib.ta_decode_noalloc(by(dq), by(dk), by(dv), sl, by(do), by(dl), int(chunk), s))
     return out, lse
 
 

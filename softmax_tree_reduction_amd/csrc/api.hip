@@ -402,6 +402,43 @@ int launch_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, co
                        out_st, lse ? static_cast<float*>(lse->data) : nullptr, lse_st, merge_scratch, st);
 }
 
+// ---- the allocation-free variant of ta_decode --------------------------------
+// Its partial states and merge scratch live in this file-scope device array
+// instead of library workspace, for callers that cannot allocate. Each device the
+// library runs on holds its own copy, at its own address, until the process ends.
+// In host code `scratch` is only a stand-in for the symbol: kernels get the device
+// address that hipGetSymbolAddress returns for the current device, never the name.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The device address of `scratch` on the current device, looked up once per device
+// with that device current. Returns TA_OK and sets *ptr, or a TA_ERR_HIP failure.
+int noalloc_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(TA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> g(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (scratch)");
+        if (!p) return fail(TA_ERR_HIP, "hipGetSymbolAddress (scratch) returned NULL");
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return TA_OK;
+}
+
+// Serialises the enqueueing of allocation-free calls per device, so that two host
+// threads calling on one stream enqueue their kernels back to back.
+std::mutex& noalloc_mutex(int dev) {
+    static std::mutex mus[64];
+    return mus[(unsigned)dev % 64];
+}
+
 }  // namespace
 
 extern "C" {
@@ -463,6 +500,29 @@ int ta_decode(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const 
     CallWorkspace ws(st);
     if ((rc = ws.acquire(plan.total_bytes)) != TA_OK) return rc;
     if ((rc = launch_decode(q, k, v, seqlens, out, lse, chunk, s, plan, ws.get(), st)) != TA_OK) return rc;
+    return ok();
+}
+
+int ta_decode_noalloc(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v, const int32_t* seqlens,
+                      const ta_tensor* out, const ta_tensor* lse, int32_t chunk, void* stream) {
+    DecodeShape s;
+    DecodePlan plan;
+    int rc;
+    if ((rc = check_decode(q, k, v, out, lse, chunk, &s, &plan)) != TA_OK) return rc;
+    if (plan.total_bytes > kNoAllocScratchBytes)
+        return fail(TA_ERR_UNSUPPORTED,
+                    "ta_decode_noalloc: this call needs %zu bytes of partial states and merge scratch, above the "
+                    "%zu bytes of its static scratch (use ta_decode)",
+                    plan.total_bytes, kNoAllocScratchBytes);
+    if (s.B == 0) return ok();
+    void* ws = nullptr;
+    if ((rc = noalloc_scratch(&ws)) != TA_OK) return rc;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> g(noalloc_mutex(dev));
+    if ((rc = launch_decode(q, k, v, seqlens, out, lse, chunk, s, plan, ws, static_cast<hipStream_t>(stream))) != TA_OK)
+        return rc;
     return ok();
 }
 
