@@ -637,6 +637,51 @@ def test_partial_of_an_empty_cache(dtype, d):
     assert torch.equal(co, out) and torch.equal(cl, lse)
 
 
+# ta_decode (and ta_decode_noalloc) against ta_partial + ta_combine, bit for bit, over
+# grids of one round and of several, 1 to 128 states per row, empty rows included;
+# repeated calls reuse the same workspace.
+DECODE_VS_SEPARATE_CASES = [
+    # (B, N, chunk, seqlens or None): P = 1, 2, 3, 8, 64, 65, 127, 128
+    (2, 300, 512, None), (2, 600, 300, [600, 1]), (3, 700, 256, [700, 0, 513]), (2, 4096, 512, None),
+    (2, 8192, 128, [8192, 4000]), (1, 8320, 128, None), (2, 16256, 128, [16256, 129]), (1, 16384, 128, None),
+]
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 4), (4, 4)])
+@pytest.mark.parametrize("case", DECODE_VS_SEPARATE_CASES, ids=lambda c: f"B{c[0]}N{c[1]}c{c[2]}{'r' if c[3] else ''}")
+def test_decode_equals_separate_merge_over_shapes(case, Hq, Hkv, dtype, d):
+    B, N, chunk, sl = case
+    inp = W.random_decode(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype=dtype, seed=N + chunk + Hq, seqlens=sl)
+    q, k, v, s = upload(inp)
+    s = s if sl is not None else None
+    log(f"decode vs separate merge: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} {dtype} chunk={chunk} seqlens={sl}")
+    ref_o, ref_l = _merged_by_separate_pass(q, k, v, s, chunk)
+    for rep in range(3):
+        out, lse = ta.decode(q, k, v, s, chunk=chunk)
+        na_o, na_l = ta.decode_noalloc(q, k, v, s, chunk=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"repeat {rep}: decode differs"
+        assert torch.equal(na_o, ref_o) and torch.equal(na_l, ref_l), f"repeat {rep}: decode_noalloc differs"
+    ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, dtype, what="decode vs separate merge")
+
+
+@pytest.mark.parametrize("N,chunk", [(262144, 4096), (524288, 8192)])
+def test_several_chunks_kernel_decode_equals_separate_merge(N, chunk):
+    # one workgroup per CU streaming several chunks (2 and 2 per workgroup here)
+    inp = W.random_decode(B=1, Hq=32, Hkv=8, N=N, d=128, dtype="bf16", seed=N // chunk)
+    q, k, v, _ = upload(inp)
+    log(f"several chunks per workgroup: N={N} chunk={chunk}")
+    ref_o, ref_l = _merged_by_separate_pass(q, k, v, None, chunk)
+    for _ in range(2):
+        out, lse = ta.decode(q, k, v, None, chunk=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+    ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", what=f"N={N}")
+
+
 def test_shapes_alternate_on_one_stream_and_a_second_stream():
     # different head-group counts and partial counts reuse one stream's workspace; a
     # second stream gets its own
