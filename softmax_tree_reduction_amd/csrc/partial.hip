@@ -60,9 +60,13 @@ namespace {
 
 // Most chunks one workgroup of the several-chunks kernel streams. Its LDS holds one
 // set of wave states per chunk until the end, slots x 4 waves x GT x D floats: 128 KiB
-// at 16 slots with GT = 4 or 8 slots with GT = 8 (d = 128), of the 160 KiB a CU has.
+// at 16 slots with GT = 4 (d = 128), of the 160 KiB a CU has. Workgroups of 8 heads
+// do not take several chunks: that kernel needs 256 VGPRs and spills into AGPRs, and
+// measured 19-22% slower than the per-chunk grid on GQA 8:1 shapes where it applied
+// (64 query heads, 8 KV heads; 320k-768k tokens, chunks 2048-8192, 3 and 5 chunks
+// per workgroup, d = 64 and 128).
 template <int GT>
-constexpr int max_chunks_per_wg() { return GT <= 4 ? 16 : 8; }
+constexpr int max_chunks_per_wg() { return GT <= 4 ? 16 : 0; }
 
 // Shortest stream (tokens per workgroup) for which a workgroup takes several chunks.
 constexpr int64_t kMultiMinTokens = 8192;
@@ -637,14 +641,16 @@ hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hip
     // of NW blocks, so that every wave reaches each chunk's end at the same step.
     constexpr int BT = (kWave / (D / Storage<T>::kElems)) * TPL;
     const int64_t cpw = cus > 0 && wgs % cus == 0 ? wgs / cus : 0;
-    const int cap = cpw >= 2 ? per_chunk_capacity<T, D, GT, NW, TPL, NBUF>() : 0;
-    if (!p.seqlens && p.N > 0 && p.N % p.chunk == 0 && p.chunk % (BT * NW) == 0 && cpw >= 2 &&
-        cpw <= max_chunks_per_wg<GT>() && n_chunks % cpw == 0 && cpw * p.chunk >= kMultiMinTokens && cap > 0 &&
-        cpw % cap != 0) {
-        dim3 gm((unsigned)((n_chunks + cpw - 1) / cpw), Hq / GT, B);
-        hipLaunchKernelGGL((partial_kernel_multi<T, D, GT, NW, TPL, NBUF>), gm, dim3(NW * kWave), 0, stream, q,
-                           n_chunks, (int)cpw);
-        return hipGetLastError();
+    const int cap = cpw >= 2 && max_chunks_per_wg<GT>() > 0 ? per_chunk_capacity<T, D, GT, NW, TPL, NBUF>() : 0;
+    if constexpr (max_chunks_per_wg<GT>() > 0) {
+        if (!p.seqlens && p.N > 0 && p.N % p.chunk == 0 && p.chunk % (BT * NW) == 0 && cpw >= 2 &&
+            cpw <= max_chunks_per_wg<GT>() && n_chunks % cpw == 0 && cpw * p.chunk >= kMultiMinTokens && cap > 0 &&
+            cpw % cap != 0) {
+            dim3 gm((unsigned)((n_chunks + cpw - 1) / cpw), Hq / GT, B);
+            hipLaunchKernelGGL((partial_kernel_multi<T, D, GT, NW, TPL, NBUF>), gm, dim3(NW * kWave), 0, stream, q,
+                               n_chunks, (int)cpw);
+            return hipGetLastError();
+        }
     }
     if (NWS != NW && wgs < cus)
         hipLaunchKernelGGL((partial_kernel<T, D, GT, NWS, TPL, NBUF>), grid, dim3(NWS * kWave), 0, stream, q);

@@ -961,16 +961,16 @@ def test_suggest_chunk_reads_the_device():
 @pytest.mark.parametrize("B,per_cu,dtype,d,Hkv", [
     (1, 4, "bf16", 128, 8), (1, 8, "bf16", 128, 8), (2, 4, "bf16", 128, 8), (1, 4, "bf16", 64, 8),
     (1, 5, "f32", 128, 8), (2, 4, "f32", 64, 8), (1, 2, "bf16", 128, 8), (3, 6, "bf16", 128, 8),
-    (1, 8, "bf16", 128, 4), (1, 4, "f32", 128, 4),  # 8 query heads per workgroup: the largest instance
+    (1, 8, "bf16", 128, 4), (1, 4, "f32", 128, 4),  # 8 query heads per workgroup: per-chunk kernel either way
     (4, 16, "bf16", 128, 8), (1, 16, "bf16", 64, 8),  # 16 chunks per workgroup
 ])
 def test_several_chunks_per_workgroup_are_bitwise_the_per_chunk_states(B, per_cu, dtype, d, Hkv):
     # Without seqlens, rows of whole chunks in a grid of exactly 4 to 16 rounds of CUs
-    # (8 with 8 query heads per workgroup) go to the kernel that streams several chunks
-    # per workgroup; full-length seqlens
-    # take the per-chunk kernel over the same tokens. Every state, and ta_decode's
-    # result, must be the same bits. 2 rounds, and B = 3 at 6 rounds (64 chunks per
-    # row, no multiple of 6), stay on the per-chunk kernel.
+    # go to the kernel that streams several chunks per workgroup (not with 8 query heads
+    # per workgroup, which keep the per-chunk grid); full-length seqlens take the
+    # per-chunk kernel over the same tokens. Every state, and ta_decode's result, must
+    # be the same bits. 2 rounds, and B = 3 at 6 rounds (64 chunks per row, no multiple
+    # of 6), stay on the per-chunk kernel.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     Hq, chunk = 32, 2048
     groups = Hq // min(8, Hq // Hkv)  # workgroups per chunk of a sequence (Hq / Hkv is 4 or 8 here)
