@@ -493,6 +493,36 @@ def main() -> int:
     print(f"bench: {args.steps} steps, {ms_step * 1e3:.1f} us/step (host wall {wall / args.steps * 1e6:.1f} us/step)",
           file=sys.stderr, flush=True)
 
+    # ---- the same steps replayed from one captured graph through the allocation-free
+    # entry point (what a caller that captures its decode loop gets; reported apart)
+    graph_us = None
+    try:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            ta.decode_noalloc(q, ks[0], vs[0], sl, chunk=chunk, out=out, lse=lse)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                ta.decode_noalloc(q, ks[i % copies], vs[i % copies], sl, chunk=chunk, out=out, lse=lse)
+        graph.replay()
+        torch.cuda.synchronize()
+        # capturing and instantiating the graph left the device idle: settle it again
+        settle_and_read_ceiling(ta, torch, dev, stream, args.settle_ms)
+        reps = []
+        for _ in range(3):  # the median of three timed replays
+            ev0.record(stream)
+            graph.replay()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            reps.append(ev0.elapsed_time(ev1) / args.steps * 1e3)
+        graph_us = round(sorted(reps)[1], 2)
+        del graph
+    except ta.TreeAttnError as e:  # a step larger than the static scratch
+        print(f"bench: no graph replay ({e})", file=sys.stderr, flush=True)
+
     # ---- the same step at the chunk ta_suggest_chunk gives (reported apart, not `value`)
     # (opt-in: the default run launches the partial kernel at the workload's chunk only,
     # so a kernel trace of it averages one grid)
@@ -577,6 +607,7 @@ def main() -> int:
                              "note": "single steps from a separate pass with an event recorded after every step; "
                                      "each event adds its own few µs, so these run longer than the timed loop"},
         "us_per_step_warm": round(ms_warm * 1e3, 2),
+        "us_per_step_graph_noalloc": graph_us,
         "suggested_chunk": alt,
         "read_ceiling": {"value": round(ceiling, 1), "unit": "GB/s", "kernel": "ta_stream_read",
                          "bytes_per_launch": 2**30, "step_pct_of_ceiling": round(100 * gbs / ceiling, 2)},
