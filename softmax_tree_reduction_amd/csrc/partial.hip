@@ -71,6 +71,15 @@ constexpr int max_chunks_per_wg() { return GT <= 4 ? 16 : 0; }
 // Shortest stream (tokens per workgroup) for which a workgroup takes several chunks.
 constexpr int64_t kMultiMinTokens = 8192;
 
+// LDS a launch of the per-chunk kernel reserves beyond its own, unused, so that at
+// most two workgroups share a CU (with the kernel's own 8 KiB at GT = 4 and d = 128,
+// two take 137 KiB of the CU's 160 KiB, three would need 205). Ragged grids of many
+// rounds (seqlens given, more than 8 workgroups per CU on the grid) streamed
+// 0.2-1.1% faster with two resident workgroups than with the three the registers
+// allow (bf16, d = 128, GQA 4:1: batches of 2 to 64 sequences, chunks 512 to 4096),
+// and never slower.
+constexpr unsigned kTwoPerCuLds = 60u << 10;
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <typename T>
@@ -652,10 +661,12 @@ hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hip
             return hipGetLastError();
         }
     }
+    constexpr bool kMeasuredTwoPerCu = std::is_same<T, uint16_t>::value && D == 128 && GT <= 4;
+    const unsigned reserve = kMeasuredTwoPerCu && p.seqlens && wgs > 8 * (int64_t)cus ? kTwoPerCuLds : 0u;
     if (NWS != NW && wgs < cus)
         hipLaunchKernelGGL((partial_kernel<T, D, GT, NWS, TPL, NBUF>), grid, dim3(NWS * kWave), 0, stream, q);
     else
-        hipLaunchKernelGGL((partial_kernel<T, D, GT, NW, TPL, NBUF>), grid, dim3(NW * kWave), 0, stream, q);
+        hipLaunchKernelGGL((partial_kernel<T, D, GT, NW, TPL, NBUF>), grid, dim3(NW * kWave), reserve, stream, q);
     return hipGetLastError();
 }
 
