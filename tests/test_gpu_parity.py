@@ -137,7 +137,9 @@ def test_partial_states_match_oracle_windows():
 def test_ragged_chunk_orders_match_oracle_windows(P):
     # Ragged grids with 8 head groups per sequence and at most 32 chunks per row are
     # walked chunk-major, the others with the chunk index fastest (rotated per row
-    # when the row has a multiple of 8 chunks): every state must land in its own slot
+    # when the row has a multiple of 8 chunks): every state must land in its own slot.
+    # At P = 64 the grid (2560 workgroups) has more than 8 per CU of a 256-CU device,
+    # so the launch also reserves LDS to keep two workgroups per CU.
     chunk = 64
     N = P * chunk
     lens = [N, min(700, N - 3), N - 1, 0, 65]
