@@ -32,7 +32,8 @@
 //    is written.
 //  - A chunk past its sequence's end does no work. Its empty state, when the
 //    caller reads it, is written by the row's non-empty workgroups. Grids of many
-//    rounds of workgroups write the states with nontemporal stores.
+//    rounds of workgroups write the states with nontemporal stores, and ragged ones
+//    among them run two workgroups per CU instead of three.
 #include <atomic>
 #include <type_traits>
 
@@ -637,7 +638,7 @@ hipError_t launch_typed(const PartialParams& p, int B, int Hq, int n_chunks, hip
     // states in L2 for the merge.
     PartialParams q = p;
     q.stream_states = wgs > 8 * (int64_t)cus ? 1 : 0;
-    // A grid of a whole number k (2 to 16, 8 with GT = 8) of workgroups per CU streams
+    // A grid of a whole number k (2 to 16; GT of at most 4) of workgroups per CU streams
     // 0.4-2.2% faster as one workgroup per CU taking k consecutive chunks in one
     // stream, when that stream is at least 8192 tokens long (measured with k = 2 to
     // 16 on 256k to 4 x 512k tokens) -- unless the per-chunk grid itself fills whole
