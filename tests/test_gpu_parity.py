@@ -133,18 +133,21 @@ def test_partial_states_match_oracle_windows():
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
-@pytest.mark.parametrize("P", [8, 32, 33, 64])
-def test_ragged_chunk_orders_match_oracle_windows(P):
-    # Ragged grids with 8 head groups per sequence and at most 32 chunks per row are
-    # walked chunk-major, the others with the chunk index fastest (rotated per row
-    # when the row has a multiple of 8 chunks): every state must land in its own slot.
-    # At P = 64 the grid (2560 workgroups) has more than 8 per CU of a 256-CU device,
-    # so the launch also reserves LDS to keep two workgroups per CU.
+@pytest.mark.parametrize("B,P", [(5, 8), (5, 32), (5, 33), (5, 64), (64, 33), (72, 32), (72, 33), (72, 64)])
+def test_ragged_chunk_orders_match_oracle_windows(B, P):
+    # Ragged grids of at most 64 sequences take the compacted order (the workgroups
+    # with work first; those after them write the empty states of sequences without
+    # tokens). Larger ones with 8 head groups per sequence and at most 32 chunks per
+    # row are walked chunk-major, the others with the chunk index fastest (rotated per
+    # row when the row has a multiple of 8 chunks). Every state must land in its own
+    # slot. At B = 5, P = 64 the grid (2560 workgroups) has more than 8 per CU of a
+    # 256-CU device, so the launch also reserves LDS to keep two workgroups per CU.
     chunk = 64
     N = P * chunk
-    lens = [N, min(700, N - 3), N - 1, 0, 65]
-    inp = W.random_decode(B=5, Hq=32, Hkv=8, N=N, d=128, dtype="bf16", seed=P, seqlens=lens)
-    log(f"chunk orders: P={P} N={N} lens={lens}")
+    base = [N, min(700, N - 3), N - 1, 0, 65]
+    lens = [base[b % 5] if b % 3 else (b * 7919) % (N + 1) for b in range(B)]
+    inp = W.random_decode(B=B, Hq=32, Hkv=8, N=N, d=128, dtype="bf16", seed=P + B, seqlens=lens)
+    log(f"chunk orders: B={B} P={P} N={N} lens={lens[:8]}...")
     q, k, v, sl = upload(inp)
     po, pl = ta.partial(q, k, v, sl, chunk=chunk)
     out, lse = ta.decode(q, k, v, sl, chunk=chunk)
@@ -152,9 +155,9 @@ def test_ragged_chunk_orders_match_oracle_windows(P):
     po, pl = po.cpu().numpy(), pl.cpu().numpy()
     for i in range(P):
         ro, rl = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens, t_begin=i * chunk, t_end=(i + 1) * chunk)
-        assert_close(po[:, :, i], pl[:, :, i], ro, rl, "bf16", what=f"P={P} state {i}")
+        assert_close(po[:, :, i], pl[:, :, i], ro, rl, "bf16", what=f"B={B} P={P} state {i}")
     ref_o, ref_l = oracle.decode(inp.q, inp.k, inp.v, inp.seqlens)
-    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "bf16", what=f"P={P} decode")
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "bf16", what=f"B={B} P={P} decode")
 
 
 # tokens in one wave-wide block: 4 tokens per lane x the rows a wave-wide load covers
