@@ -207,7 +207,10 @@ int ta_partial(const ta_tensor* q, const ta_tensor* k, const ta_tensor* v,
  * `bytes` bytes of device memory at `buf` once, with 16-byte nontemporal loads
  * (the width and cache policy of the partial kernel's K and V loads), and
  * computes nothing from them.
- * Timing it gives the device's practical read ceiling for this access.
+ * Timing it gives the device's practical read ceiling for this access. Buffers
+ * of up to 256 KiB per compute unit are read by one round of workgroups of
+ * 32 KiB each (every load in flight at once); larger ones by one workgroup per
+ * compute unit, each streaming one contiguous slice.
  *
  *   buf     device pointer, 16-byte aligned; bytes >= 0, a multiple of 16
  *   sink    device pointer to one uint32 that the probe may overwrite

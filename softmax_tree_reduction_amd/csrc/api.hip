@@ -602,10 +602,7 @@ int ta_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream)
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "stream_read: device query");
     const int64_t n16 = bytes / 16;
-    // one workgroup per CU, each streaming one contiguous slice: the fastest of the
-    // shapes measured (1 to 8 workgroups per CU, 256 to 1024 threads)
-    const int64_t grid = (int64_t)cus < n16 ? (int64_t)cus : n16;
-    if ((e = ta::launch_stream_read(buf, n16, sink, (int)grid, static_cast<hipStream_t>(stream))) != hipSuccess)
+    if ((e = ta::launch_stream_read(buf, n16, sink, cus, static_cast<hipStream_t>(stream))) != hipSuccess)
         return hip_fail(e, "stream_read kernel launch");
     return ok();
 }

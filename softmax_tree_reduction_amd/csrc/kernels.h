@@ -62,8 +62,9 @@ hipError_t launch_partial(const PartialParams& p, Dtype dt, int d, int heads_per
 // one pass, no workspace; p.seqlens is not read.
 hipError_t launch_combine_chain(const CombineParams& p, int d, int B, int H, hipStream_t stream);
 
-// The read-bandwidth probe: `grid` workgroups stream n16 16-byte items from buf.
-hipError_t launch_stream_read(const void* buf, int64_t n16, uint32_t* sink, int grid, hipStream_t stream);
+// The read-bandwidth probe: streams n16 16-byte items from buf, in a launch shape
+// chosen from the size and the device's `cus` compute units.
+hipError_t launch_stream_read(const void* buf, int64_t n16, uint32_t* sink, int cus, hipStream_t stream);
 
 // Leaves per workgroup of the arity-K merge: the largest power of K it takes.
 int combine_k_span(int d, int arity);

@@ -69,6 +69,27 @@ __device__ __forceinline__ Leaves<R> load_leaves(const float* po, int64_t po_sp,
     const int cg = threadIdx.x % CG;
     const int base = first + (int)(threadIdx.x / CG) * R;
     Leaves<R> lv;
+    if constexpr (R % 4 == 0) {
+        // Every leaf of the workgroup holds data and the lse are contiguous and 16-byte
+        // aligned (the same decision in every lane): one 64-bit product per thread, then
+        // wave-uniform leaf strides, and the lse of 4 consecutive leaves in one load.
+        constexpr int S = NT / CG;
+        if (first + S * R <= valid && pl_sp == 1 && (reinterpret_cast<uintptr_t>(pl + first) & 15u) == 0) {
+            const float* op = po + (int64_t)base * po_sp + 4 * cg;
+            const float* lp = pl + base;
+#pragma unroll
+            for (int r = 0; r < R; r += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(lp + r);
+                lv.lse[r] = v.x;
+                lv.lse[r + 1] = v.y;
+                lv.lse[r + 2] = v.z;
+                lv.lse[r + 3] = v.w;
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) lv.o[r] = *reinterpret_cast<const float4*>(op + (int64_t)r * po_sp);
+            return lv;
+        }
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int i = base + r;
