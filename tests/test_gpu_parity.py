@@ -133,20 +133,23 @@ def test_partial_states_match_oracle_windows():
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
-@pytest.mark.parametrize("B,P", [(5, 8), (5, 32), (5, 33), (5, 64), (64, 33), (72, 32), (72, 33), (72, 64)])
-def test_ragged_chunk_orders_match_oracle_windows(B, P):
+@pytest.mark.parametrize("B,P,Hq,Hkv,d,chunk", [
+    (5, 8, 32, 8, 128, 64), (5, 32, 32, 8, 128, 64), (5, 33, 32, 8, 128, 64), (5, 64, 32, 8, 128, 64),
+    (64, 33, 32, 8, 128, 64), (72, 32, 32, 8, 128, 64), (72, 64, 32, 8, 128, 64), (200, 33, 32, 8, 128, 32),
+    (520, 32, 8, 8, 64, 16), (520, 33, 8, 8, 64, 16), (520, 40, 8, 8, 64, 16)])
+def test_ragged_chunk_orders_match_oracle_windows(B, P, Hq, Hkv, d, chunk):
     # Ragged grids of at most 64 sequences take the compacted order (the workgroups
     # with work first; those after them write the empty states of sequences without
     # tokens). Larger ones with 8 head groups per sequence and at most 32 chunks per
     # row are walked chunk-major, the others with the chunk index fastest (rotated per
     # row when the row has a multiple of 8 chunks). Every state must land in its own
-    # slot. At B = 5, P = 64 the grid (2560 workgroups) has more than 8 per CU of a
-    # 256-CU device, so the launch also reserves LDS to keep two workgroups per CU.
-    chunk = 64
+    # slot. At B = 5,
+    # P = 64 the grid (2560 workgroups) has more than 8 per CU of a 256-CU device, so
+    # the launch also reserves LDS to keep two workgroups per CU.
     N = P * chunk
     base = [N, min(700, N - 3), N - 1, 0, 65]
     lens = [base[b % 5] if b % 3 else (b * 7919) % (N + 1) for b in range(B)]
-    inp = W.random_decode(B=B, Hq=32, Hkv=8, N=N, d=128, dtype="bf16", seed=P + B, seqlens=lens)
+    inp = W.random_decode(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype="bf16", seed=P + B, seqlens=lens)
     log(f"chunk orders: B={B} P={P} N={N} lens={lens[:8]}...")
     q, k, v, sl = upload(inp)
     po, pl = ta.partial(q, k, v, sl, chunk=chunk)
