@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
     if (p.seqlens) {
         int n = p.seqlens[b];
         n = n < 0 ? 0 : (n > p.N ? p.N : n);
-        const int pb = (int)(((int64_t)n + p.chunk - 1) / p.chunk);
+        const int pb = (int)(((unsigned)n + (unsigned)p.chunk - 1u) / (unsigned)p.chunk);  // n <= N <= INT32_MAX - chunk
         valid = pb < valid ? pb : valid;
     }
     const float* po = p.po + (int64_t)b * p.po_sb + (int64_t)h * p.po_sh;
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void combine_k_kernel(CombineParams p, in
     if (p.seqlens) {
         int n = p.seqlens[b];
         n = n < 0 ? 0 : (n > p.N ? p.N : n);
-        const int pb = (int)(((int64_t)n + p.chunk - 1) / p.chunk);
+        const int pb = (int)(((unsigned)n + (unsigned)p.chunk - 1u) / (unsigned)p.chunk);  // n <= N <= INT32_MAX - chunk
         valid = pb < valid ? pb : valid;
     }
     const int first = grp * span;

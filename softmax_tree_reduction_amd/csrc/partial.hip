@@ -536,7 +536,7 @@ __device__ __forceinline__ Item compact_item(const PartialParams& p, uint64_t L,
         nl = p.seqlens[lane];
         nl = nl < 0 ? 0 : (nl > p.N ? p.N : nl);
     }
-    const int nbl = (int)(((int64_t)nl + p.chunk - 1) / p.chunk);
+    const int nbl = (int)(((unsigned)nl + (unsigned)p.chunk - 1u) / (unsigned)p.chunk);
     int incl = nbl;  // chunks holding tokens in sequences 0 .. lane
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -618,7 +618,8 @@ __global__ __launch_bounds__(NW * kWave) void partial_kernel(PartialParams p) {
     // covers chunks j + nb, j + 2 nb, ...): an empty workgroup that stayed to store
     // 2 KB would hold its compute-unit slot for a whole write latency. A row with no
     // tokens at all has no such workgroup and writes its own.
-    const int64_t nb = ((int64_t)n + p.chunk - 1) / p.chunk;
+    // in 32 bits: n <= N, and the launcher refuses N > INT32_MAX - chunk
+    const int64_t nb = ((unsigned)n + (unsigned)p.chunk - 1u) / (unsigned)p.chunk;
     float* po_row = p.po + (int64_t)b * p.po_sb + (int64_t)h0 * p.po_sh;
     float* pl_row = p.plse + (int64_t)b * p.pl_sb + (int64_t)h0 * p.pl_sh;
     if (chunk_idx >= nb) {
